@@ -1,0 +1,30 @@
+"""CPU oracle for Decode Context Parallel (DCP) decode attention.
+
+THIS PACKAGE IS TEST INFRASTRUCTURE. Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import it.
+The product path (``sequence_sharded_paged_amd``) never imports, calls or links
+anything here, and this package imports nothing from the product path: the two
+share no code.
+
+What it computes, each function citing the passage it follows:
+
+* ``formats``   - exact decoding of the stored KV formats (fp32, bf16, OCP
+                  fp8 e4m3fn) into float64.
+* ``layout``    - brute-force slot mapper: the four per-token layout formulas of
+                  "Decode Context Parallel (DCP)" (vLLM Ascend design doc),
+                  section "KV-cache layout", evaluated literally, plus a running
+                  per-rank counter; local sequence lengths are the counters'
+                  final values.
+* ``attention`` - plain full-softmax decode attention over the *unsharded*
+                  sequence in float64, the per-rank partial (O, LSE) over the
+                  tokens a rank owns, and the log-sum-exp merge with an
+                  attention sink applied once ("DeepSeek V4.1 context
+                  parallelism", section "Decode computation").
+
+Every function here is pinned by ``-m "not gpu"`` tests against something other
+than itself (hand-derived worked example, closed forms, invariants, torch's
+float64 scaled-dot-product attention, torch's float8 decoding, brute force).
+No function is "parity unpinned".
+"""
+
+from . import formats, layout, attention  # noqa: F401

@@ -1,0 +1,17 @@
+"""Seeded synthetic inputs for DCP decode attention.
+
+This module generates inputs only: sequence lengths, block tables, queries,
+canonical (unsharded, request-contiguous) keys and values in their stored
+format, fp8 scales and attention sinks. It holds none of the method's
+arithmetic (no slot mapping, no attention, no merge), so the CPU oracle and
+the HIP path can both consume what it produces without sharing code.
+
+The workloads stand in for the agentic long-context trace described in
+"Efficient Decode Context Parallelism with vLLM for Long Context Workloads",
+section 2.1 (median input ~67k tokens, bimodal: about half at 64k and above
+with a tail to ~1M, ~18% under 8k, ~8% over 128k). None of that trace's items
+are used; only its length statistics shape the mixtures below.
+"""
+
+from .configs import WORKLOADS, Workload, get_workload  # noqa: F401
+from .generate import Case, make_case  # noqa: F401

@@ -1,0 +1,96 @@
+"""The five synthetic decode workloads, named by what they are.
+
+Length laws ("k" = 1024 tokens):
+* ``loguniform(a, b)``: L = floor(exp(U(ln a, ln b))), clipped to [a, b];
+* ``uniform(a, b)``: integer uniform on [a, b];
+* mixtures: bin counts by largest remainder, then a seeded shuffle.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+K = 1024
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim_k: int
+    head_dim_v: int
+    kv_format: str            # "fp32" | "bf16" | "fp8_e4m3"
+    q_format: str             # "fp32" | "bf16"
+    block_size: int
+    dcp_size: int
+    interleave: int
+    # list of (count, law, a, b); law in {"fixed", "loguniform", "uniform"}
+    lengths: tuple = ()
+    mla: bool = False         # value = first head_dim_v entries of the key row
+    sink: bool = False        # per-query-head sink logit ~ N(0, 1)
+    out_format: str = "fp32"  # merged output format
+    description: str = ""
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim_k)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def kv_bytes_per_token(self) -> int:
+        elem = {"fp32": 4, "bf16": 2, "fp8_e4m3": 1}[self.kv_format]
+        if self.mla:
+            return self.num_kv_heads * self.head_dim_k * elem
+        return self.num_kv_heads * (self.head_dim_k + self.head_dim_v) * elem
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload(
+            name="gqa_fp32_tiny", seed=1, batch=2, num_q_heads=8, num_kv_heads=2,
+            head_dim_k=64, head_dim_v=64, kv_format="fp32", q_format="fp32",
+            block_size=16, dcp_size=2, interleave=1,
+            lengths=((1, "fixed", 37, 37), (1, "fixed", 100, 100)),
+            description="tiny GQA decode, fp32, 2 requests of 37 and 100 tokens"),
+        Workload(
+            name="gqa_bf16_32k", seed=2, batch=32, num_q_heads=32, num_kv_heads=8,
+            head_dim_k=128, head_dim_v=128, kv_format="bf16", q_format="bf16",
+            block_size=16, dcp_size=4, interleave=1,
+            lengths=((32, "loguniform", 1 * K, 32 * K),),
+            out_format="bf16",
+            description="GQA decode, bf16 KV, 32 requests log-uniform 1k-32k"),
+        Workload(
+            name="mla_bf16_bimodal", seed=3, batch=64, num_q_heads=128, num_kv_heads=1,
+            head_dim_k=576, head_dim_v=512, kv_format="bf16", q_format="bf16",
+            block_size=64, dcp_size=8, interleave=1,
+            lengths=((30, "loguniform", 1 * K, 64 * K), (34, "loguniform", 64 * K, 256 * K)),
+            mla=True, out_format="bf16",
+            description="MLA latent decode, bf16, 64 requests, 47% 1k-64k / 53% 64k-256k"),
+        Workload(
+            name="mla_bf16_longtail_sink", seed=4, batch=4, num_q_heads=128, num_kv_heads=1,
+            head_dim_k=576, head_dim_v=512, kv_format="bf16", q_format="bf16",
+            block_size=64, dcp_size=8, interleave=64,
+            lengths=((4, "uniform", 512 * K, 1024 * K),),
+            mla=True, sink=True, out_format="bf16",
+            description="MLA long-tail decode, bf16, 4 requests 512k-1M, attention sink"),
+        Workload(
+            name="gqa_fp8_binned", seed=5, batch=256, num_q_heads=64, num_kv_heads=8,
+            head_dim_k=128, head_dim_v=128, kv_format="fp8_e4m3", q_format="bf16",
+            block_size=64, dcp_size=8, interleave=64,
+            lengths=((46, "loguniform", 1 * K, 8 * K), (74, "loguniform", 8 * K, 64 * K),
+                     (115, "loguniform", 64 * K, 128 * K), (21, "loguniform", 128 * K, 256 * K)),
+            out_format="bf16",
+            description="GQA decode, fp8 e4m3 KV with per-head scales, 256 requests, binned 1k-256k"),
+    ]
+}
+
+
+def get_workload(name: str) -> Workload:
+    if name not in WORKLOADS:
+        raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
+    return WORKLOADS[name]

@@ -1,0 +1,180 @@
+"""Seeded generation of one decode batch in its stored formats.
+
+Streams: ``numpy.random.SeedSequence(entropy=seed, spawn_key=(stream, i))``
+with stream 0 = lengths, 1 = block permutation, 2 = q, 3 = K, 4 = V,
+5 = fp8 scales and sinks, 6 = needles. K and V are drawn per request, in
+canonical (request-contiguous) token order, with a torch generator on the
+requested device, so large batches are produced in device memory; the stored
+values are what both the oracle (after a copy to the host) and the GPU path
+read.
+
+Values: q, K, V ~ N(0, 1). bf16 is round-to-nearest-even from the float32
+sample. fp8 e4m3 stores ``clamp(x / scale[h], -448, 448)`` rounded to nearest
+even, with ``scale[h] = (6 / 448) * 2**U(0, 2)`` drawn per KV head for K and,
+independently, for V (6 stands for the largest |x| expected from N(0, 1) at
+these sizes; the random power of two makes every head's scale different).
+Sinks ~ N(0, 1) per query head.
+
+Block table: request b needs ``ceil(L_b / (block_size * dcp_size))`` virtual
+blocks; physical block ids are a seeded random permutation of
+``0..num_blocks-1`` handed out to (request, virtual block) in order; unused
+entries hold -1.
+"""
+
+from dataclasses import dataclass
+import math
+
+import numpy as np
+import torch
+
+from .configs import Workload
+
+LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES = range(7)
+
+TORCH_FORMAT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
+
+
+def _seed(seed: int, stream: int, index: int = 0) -> int:
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(stream, index))
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def _rng(seed: int, stream: int, index: int = 0) -> np.random.Generator:
+    return np.random.default_rng(_seed(seed, stream, index))
+
+
+def sample_lengths(w: Workload) -> np.ndarray:
+    rng = _rng(w.seed, LENGTHS)
+    out = []
+    for count, law, a, b in w.lengths:
+        if law == "fixed":
+            out += [a] * count
+        elif law == "uniform":
+            out += list(rng.integers(a, b + 1, size=count))
+        elif law == "loguniform":
+            x = np.exp(rng.uniform(math.log(a), math.log(b), size=count))
+            out += list(np.clip(np.floor(x), a, b).astype(np.int64))
+        else:
+            raise ValueError(law)
+    lens = np.asarray(out, dtype=np.int64)
+    if len(w.lengths) > 1 and any(law != "fixed" for _, law, _, _ in w.lengths):
+        lens = lens[rng.permutation(lens.shape[0])]
+    return lens.astype(np.int32)
+
+
+def make_block_table(w: Workload, seq_lens: np.ndarray, extra_vblocks: int = 0):
+    span = w.block_size * w.dcp_size
+    nvb = [(int(L) + span - 1) // span for L in seq_lens]
+    num_blocks = int(sum(nvb))
+    max_vb = max(nvb + [1]) + extra_vblocks
+    perm = _rng(w.seed, BLOCKPERM).permutation(num_blocks).astype(np.int32)
+    table = np.full((len(seq_lens), max_vb), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(nvb):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    return table, max(num_blocks, 1)
+
+
+def _randn(shape, seed: int, device) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def _scales(w: Workload, which: int) -> np.ndarray:
+    rng = _rng(w.seed, SCALES, which)
+    return ((6.0 / 448.0) * np.exp2(rng.uniform(0.0, 2.0, size=w.num_kv_heads))).astype(np.float32)
+
+
+def _store(x: torch.Tensor, fmt: str, scale=None) -> torch.Tensor:
+    if fmt == "fp8_e4m3":
+        s = torch.as_tensor(scale, device=x.device).view(1, -1, 1)
+        return (x / s).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return x.to(TORCH_FORMAT[fmt])
+
+
+@dataclass
+class Case:
+    workload: Workload
+    seq_lens: np.ndarray          # [B] int32
+    block_table: np.ndarray       # [B, max_vblocks] int32, -1 = unused
+    num_blocks: int               # physical blocks per rank pool
+    q: torch.Tensor               # [B, Hq, Dk] in q_format
+    k: list                       # per request [L, Hkv, Dk] in kv_format
+    v: list                       # per request [L, Hkv, Dv] in kv_format, or None (MLA)
+    k_scale: np.ndarray           # [Hkv] float32 (fp8) or None
+    v_scale: np.ndarray           # [Hkv] float32 (fp8) or None
+    sink: np.ndarray              # [Hq] float32 or None
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def kv_bytes(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum()) * self.workload.kv_bytes_per_token()
+
+
+def make_case(w: Workload, device="cpu", seq_lens=None, extra_vblocks: int = 0,
+              needles: int = 0, needle_logit: float = 20.0) -> Case:
+    """Generate one batch. ``seq_lens`` overrides the workload's length law
+    (used for reduced-size parity cases with the workload's geometry)."""
+    lens = sample_lengths(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    B = lens.shape[0]
+    table, num_blocks = make_block_table(w, lens, extra_vblocks)
+    q32 = _randn((B, w.num_q_heads, w.head_dim_k), _seed(w.seed, QSTREAM), device)
+    q = q32.to(TORCH_FORMAT[w.q_format])
+    k_scale = _scales(w, 0) if w.kv_format == "fp8_e4m3" else None
+    v_scale = _scales(w, 1) if w.kv_format == "fp8_e4m3" else None
+    sink = _rng(w.seed, SCALES, 2).standard_normal(w.num_q_heads).astype(np.float32) if w.sink else None
+    ks, vs = [], []
+    for b in range(B):
+        L = int(lens[b])
+        kb = _randn((L, w.num_kv_heads, w.head_dim_k), _seed(w.seed, KSTREAM, b), device)
+        vb = None
+        if not w.mla:
+            vb = _randn((L, w.num_kv_heads, w.head_dim_v), _seed(w.seed, VSTREAM, b), device)
+        if needles and L > 0:
+            _plant_needles(w, b, L, kb, q32[b], needles, needle_logit, lens)
+        ks.append(_store(kb, w.kv_format, k_scale))
+        vs.append(None if vb is None else _store(vb, w.kv_format, v_scale))
+        del kb, vb
+    return Case(w, lens, table, num_blocks, q, ks, None if w.mla else vs, k_scale, v_scale, sink)
+
+
+def needle_positions(w: Workload, b: int, L: int, count: int) -> np.ndarray:
+    """Seeded needle positions: ``count`` random ones plus the last token and
+    the first token of the last (possibly partial) block-sized chunk."""
+    rng = _rng(w.seed, NEEDLES, b)
+    pos = list(rng.integers(0, L, size=count))
+    pos += [L - 1, (L - 1) - ((L - 1) % w.block_size)]
+    return np.unique(np.asarray(pos, dtype=np.int64))
+
+
+def _plant_needles(w, b, L, kb, qb, count, logit, lens):
+    """Overwrite a few key rows so one query head of the group scores them at
+    about ``logit`` (before the fp8 scale), making the output of that head
+    close to the needle's value row."""
+    rng = _rng(w.seed, NEEDLES, 100000 + b)
+    for x in needle_positions(w, b, L, count):
+        kv = int(rng.integers(0, w.num_kv_heads))
+        h = kv * w.group + int(rng.integers(0, w.group))
+        qh = qb[h].float()
+        kb[int(x), kv] = qh * (logit / (w.softmax_scale * float(qh.norm()) ** 2))
+
+
+def stored_numpy(t: torch.Tensor) -> np.ndarray:
+    """Raw stored representation on the host: float32, uint16 (bf16 bits) or
+    uint8 (fp8 codes)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    raise TypeError(t.dtype)
+
+
+def stored_format(t: torch.Tensor) -> str:
+    return {torch.float32: "fp32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3"}[t.dtype]
