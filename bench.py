@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark: one DCP decode step on one MI355X.
+
+A step is the whole hot path over one batch already resident in HBM: every
+DCP rank's partial decode attention over its sequence shard (planner, MFMA
+attention kernel, split combine) followed by the log-sum-exp merge across the
+ranks. The batch is synthetic (seeded; lengths, geometry and value
+distributions of the named workload). Prints ONE JSON line:
+
+* ``value``   - algorithmic KV bytes of the batch / step time, in GB/s
+                (KV bytes = sum of context lengths x KV bytes per token);
+* ``roofline``- the main attention kernel alone, timed with HIP events that
+                the library records around it on the launch stream, against
+                the 8 TB/s HBM peak; ``traffic`` comes from the committed
+                rocprofv3 counter summary when it was taken on the current
+                kernel source, else null;
+* ``cpu_baseline`` - the float64 CPU oracle timed on a bounded sample of the
+                same batch (rank 0, N = 1 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU"
+DEFAULT_WORKLOAD = "gqa_fp8_binned"
+KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel"}
+KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip"}
+
+
+def kernel_family(w):
+    if w.mla:
+        return "mla"
+    if w.kv_format in ("bf16", "fp8_e4m3") and w.head_dim_k == 128:
+        return "gqa"
+    return "generic"
+
+
+def source_hash(family):
+    path = os.path.join(ROOT, "sequence_sharded_paged_amd", "csrc", KERNEL_SOURCES[family])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(family, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[family]}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(family):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s):
+    """Time the float64 oracle on a seeded sample of requests (~budget_s)."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import formats as ofmt
+    from workloads.generate import stored_format, stored_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing
+        threads = 1
+    w = case.workload
+    order = np.random.default_rng(12345).permutation(case.batch)
+    spent, kv_bytes, done = 0.0, 0, []
+    for b in order:
+        q_st = stored_numpy(case.q[b])
+        k_st = stored_numpy(case.k[b])
+        v_st = None if case.v is None else stored_numpy(case.v[b])
+        t0 = time.perf_counter()
+        q = ofmt.decode(q_st, stored_format(case.q))
+        k = ofmt.decode_kv(k_st, stored_format(case.k[b]), case.k_scale)
+        v = k[:, :, :w.head_dim_v] if v_st is None else ofmt.decode_kv(v_st, stored_format(case.v[b]),
+                                                                        case.v_scale)
+        oatt.decode_attention(q, k, v, w.softmax_scale, case.sink)
+        spent += time.perf_counter() - t0
+        kv_bytes += int(case.seq_lens[b]) * w.kv_bytes_per_token()
+        done.append(int(b))
+        if spent >= budget_s:
+            break
+    return {
+        "value": kv_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {case.batch} requests (seeded random order, "
+                   f"{sum(int(case.seq_lens[b]) for b in done)} tokens), full softmax over the unsharded "
+                   f"sequence in float64 incl. decoding the stored KV; {spent:.1f} s"),
+        "queries_per_s": len(done) / spent,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: the DCP ranks are virtual and all resident in one GPU's HBM; "
+              "runs on more than one GPU are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from tests.harness import DeviceInputs
+    from workloads import get_workload, make_case
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = get_workload(args.workload)
+    t_gen = time.perf_counter()
+    case = make_case(w, device="cuda")
+    inp = DeviceInputs(case, "cuda", fill="zero")
+    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name}: batch {case.batch}, {int(case.seq_lens.sum())} tokens, "
+          f"{case.kv_bytes() / 1e9:.3f} GB KV, inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        inp.step()
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dcp.native.dcp_profile_enable(True)
+    dcp.native.dcp_profile_collect()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        inp.step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern_ms, launches = dcp.native.dcp_profile_collect()
+    dcp.native.dcp_profile_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    kern_avg_ms = kern_ms / max(launches, 1)
+
+    kv_bytes = case.kv_bytes()
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
+    family = kernel_family(w)
+    traffic = load_traffic(family, w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": case.batch,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim_k": w.head_dim_k,
+            "head_dim_v": w.head_dim_v,
+            "kv_format": w.kv_format,
+            "block_size": w.block_size,
+            "dcp_size": w.dcp_size,
+            "interleave": w.interleave,
+            "tokens": int(case.seq_lens.astype(np.int64).sum()),
+            "kv_bytes": int(kv_bytes),
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "merged_queries_per_s": round(case.batch / (ms * 1e-3), 1),
+            "kernel": KERNEL_NAMES[family],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_avg_ms": round(kern_avg_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

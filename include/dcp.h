@@ -1,0 +1,257 @@
+/*
+ * dcp.h - C ABI of libdcp: Decode Context Parallel (DCP) decode attention on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for a paged KV cache sharded along the sequence
+ * dimension over dcp_size ranks with an interleaved layout, the slot mapping
+ * of tokens to ranks, the per-rank context lengths, each rank's partial decode
+ * attention (O, LSE) over its local shard, and the log-sum-exp merge of the
+ * partials with an optional attention sink applied once. All dcp_size virtual
+ * ranks may live on the same GPU; a per-GPU deployment passes its own rank
+ * through rank_begin / rank_count.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device; the caller owns every buffer. The library
+ *     allocates no device memory and keeps no state besides per-device
+ *     attributes and, while profiling is enabled, a pool of HIP events.
+ *   - All calls are stream-ordered on `stream` (a hipStream_t; NULL = the
+ *     null stream) and never synchronize the host.
+ *   - Arguments are validated on the host before anything is launched. On an
+ *     error nothing is launched and a negative status is returned; nothing is
+ *     printed and nothing aborts. Values that live in device memory (block
+ *     ids, lengths, positions) are the caller's contract: block ids must lie
+ *     in [0, num_blocks) wherever a kernel reads them.
+ *   - Element strides are counted in elements of the stated type.
+ */
+#ifndef DCP_H
+#define DCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  DCP_OK = 0,
+  DCP_ERR_INVALID_ARG = -1, /* a size, pointer or relation between arguments is wrong */
+  DCP_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, head dims, layout) */
+  DCP_ERR_WORKSPACE = -3,   /* workspace smaller than the size query returned */
+  DCP_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Element formats. DCP_FP8_E4M3 is the OCP 8-bit E4M3 format without
+ * infinities (bias 7, max 448, S.1111.111 = NaN); fp8 values are dequantised
+ * as code * scale[kv_head]. */
+enum { DCP_F32 = 0, DCP_BF16 = 1, DCP_FP8_E4M3 = 2 };
+
+/* Kernel selection for dcp_partial_decode_attn. AUTO picks the MFMA kernel
+ * when the geometry is supported and the generic kernel otherwise; GENERIC
+ * forces the generic fp32 kernel; FAST fails with DCP_ERR_UNSUPPORTED when no
+ * MFMA kernel fits. */
+enum { DCP_ALGO_AUTO = 0, DCP_ALGO_GENERIC = 1, DCP_ALGO_FAST = 2 };
+
+/* Version of this ABI (incremented on incompatible change). */
+int dcp_abi_version(void);
+
+/* Static, human-readable text for a status code. Never NULL. */
+const char* dcp_status_string(int status);
+
+/*
+ * dcp_local_seq_lens - per-rank context-length matrix.
+ *
+ * Source: "Decode Context Parallel (DCP)" (vLLM Ascend design doc), sections
+ * "KV-cache layout" (token placement) and "Backend structure" (the per-rank
+ * context-length matrix).
+ *
+ * local_lens[b * dcp_size + r] = number of positions x in [0, seq_lens[b])
+ * whose target_rank is r, where
+ *   target_rank = ((x % (block_size * dcp_size)) / interleave) % dcp_size.
+ *
+ * seq_lens   device, [num_reqs] int32, each >= 0 (negative is read as 0)
+ * num_reqs   >= 0 (0: nothing is launched)
+ * block_size >= 1; dcp_size >= 1; interleave >= 1; block_size % interleave == 0
+ * local_lens device, [num_reqs, dcp_size] int32, row-major, rank fastest
+ * Errors: DCP_ERR_INVALID_ARG for a bad size or relation or a NULL pointer
+ * when num_reqs > 0; DCP_ERR_HIP if the launch fails.
+ */
+int dcp_local_seq_lens(const int32_t* seq_lens, int32_t num_reqs, int32_t block_size,
+                       int32_t dcp_size, int32_t interleave, int32_t* local_lens,
+                       void* stream);
+
+/*
+ * dcp_slot_mapping - where each new token's KV goes on each rank.
+ *
+ * Source: "Decode Context Parallel (DCP)", section "KV-cache layout" (a
+ * virtual block spans block_size * dcp_size tokens; the four formulas give the
+ * owner of token x; block_size % interleave == 0); "DeepSeek V4.1 context
+ * parallelism", section "Cache ownership" (writes translate virtual slots to
+ * local slots and mask non-owners).
+ *
+ * For token t with position x = positions[t] in request b = req_indices[t]:
+ *   vb    = x / (block_size * dcp_size)            (virtual block index)
+ *   owner = ((x % (block_size * dcp_size)) / interleave) % dcp_size
+ *   off   = offset of x among the tokens of virtual block vb that the owner
+ *           holds, in ascending position order
+ *         = ((x / (interleave * dcp_size)) * interleave + x % interleave) % block_size
+ *   slots[owner * num_tokens + t] = block_table[b * block_table_stride + vb] * block_size + off
+ *   slots[r * num_tokens + t]     = -1 for every other rank r.
+ * All ranks get -1 when x < 0, b is outside [0, num_reqs), vb >= max_vblocks or
+ * the block id is negative. The block table is shared by all ranks: each rank
+ * has its own pool and physical block id p means block p of that rank's pool.
+ *
+ * positions          device, [num_tokens] int64
+ * req_indices        device, [num_tokens] int32
+ * num_tokens         >= 0 (0: nothing is launched)
+ * block_table        device, int32, row b at block_table + b * block_table_stride
+ * num_reqs           rows in block_table, >= 0
+ * block_table_stride >= max_vblocks
+ * max_vblocks        >= 0, valid columns per row
+ * slots              device, [dcp_size, num_tokens] int64
+ * Errors: DCP_ERR_INVALID_ARG, DCP_ERR_HIP.
+ */
+int dcp_slot_mapping(const int64_t* positions, const int32_t* req_indices, int64_t num_tokens,
+                     const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
+                     int32_t max_vblocks, int32_t block_size, int32_t dcp_size,
+                     int32_t interleave, int64_t* slots, void* stream);
+
+/*
+ * Paged KV pools of the ranks being computed, all with the same geometry.
+ * Element (rank r, block p, kv head h, token t, dim d) of K lives at
+ *   k + r*k_stride[0] + p*k_stride[1] + h*k_stride[2] + t*k_stride[3] + d*k_stride[4]
+ * with r counted from rank_begin; likewise V with v_stride. v == NULL means V
+ * is the first head_dim_v entries of the K row (MLA: one latent vector is both
+ * key and value) and v_stride is ignored. k_scale / v_scale are device
+ * [num_kv_heads] float32 and required exactly when dtype is DCP_FP8_E4M3.
+ *
+ * The MFMA kernels read these layouts (others use the generic kernel):
+ *   GQA  bf16 / fp8, head_dim_k = head_dim_v = 128, Hq/Hkv <= 16:
+ *        K dim stride 1 and V token stride 1 ("V transposed inside a block",
+ *        [block, head, dim, token]); block_size a multiple of 16; 16-byte
+ *        aligned rows.
+ *   MLA  bf16, num_kv_heads = 1, Hq = 128, head_dim_k = 576, head_dim_v = 512,
+ *        v == NULL, K dim stride 1, 16-byte aligned rows.
+ */
+typedef struct dcp_kv_cache {
+  int32_t dtype;              /* DCP_F32 | DCP_BF16 | DCP_FP8_E4M3 */
+  int32_t num_blocks;         /* physical blocks in each rank's pool */
+  int32_t block_size;         /* tokens per physical block */
+  int32_t num_kv_heads;
+  int32_t head_dim_k;
+  int32_t head_dim_v;
+  const void* k;
+  int64_t k_stride[5];        /* rank, block, head, token, dim (elements) */
+  const void* v;              /* NULL: V aliases K[..., 0:head_dim_v] */
+  int64_t v_stride[5];
+  const float* k_scale;       /* [num_kv_heads], fp8 only, else NULL */
+  const float* v_scale;       /* [num_kv_heads], fp8 only, else NULL */
+} dcp_kv_cache_t;
+
+/*
+ * dcp_partial_decode_attn_workspace_size - bytes of device workspace that
+ * dcp_partial_decode_attn needs for these arguments (0 is possible). Host
+ * only; depends on no device state. Returns 0 and sets *status (if non-NULL)
+ * to an error code when the arguments are invalid.
+ */
+size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
+                                              int32_t q_dtype, const dcp_kv_cache_t* kv,
+                                              int32_t rank_count, int32_t algo, int* status);
+
+/*
+ * dcp_partial_decode_attn - each rank's partial decode attention over its
+ * local KV shard (GQA, and MLA with v == NULL).
+ *
+ * Source: "Decode Context Parallel (DCP)", section "Decode" (attention of the
+ * gathered query heads against the local KV-cache shard, producing partial
+ * outputs and LSE values); "Efficient Decode Context Parallelism with vLLM for
+ * Long Context Workloads", sections 1 and 5.4 (MLA's single latent KV head;
+ * GQA query heads sharing their group's KV head).
+ *
+ * For rank r in [0, rank_count) (global rank rank_begin + r), request b and
+ * query head h, with n = local_lens[b * dcp_size + rank_begin + r] and KV head
+ * g = h / (num_q_heads / num_kv_heads), over the rank-local tokens j < n
+ * (token j sits in block block_table[b * block_table_stride + j / block_size],
+ * slot j % block_size of rank r's pool):
+ *   s_j   = softmax_scale * <q[b,h,:], k_j[g,:]>
+ *   LSE   = ln sum_j exp(s_j)                       (-inf when n == 0)
+ *   O     = sum_j exp(s_j - LSE) * v_j[g,:]         (0 when n == 0)
+ * fp8 K and V are dequantised as code * k_scale[g] / v_scale[g]. Accumulation
+ * is fp32; the MFMA kernels round the softmax weights to bf16 before the
+ * value product and use the same rounded weights in the denominator.
+ *
+ * q           device, [batch, num_q_heads, head_dim_k], contiguous, q_dtype
+ *             DCP_F32 or DCP_BF16
+ * local_lens  device, [batch, dcp_size] int32 (as from dcp_local_seq_lens);
+ *             every length must be <= max_vblocks * block_size
+ * rank_begin, rank_count: 0 <= rank_begin, 1 <= rank_count,
+ *             rank_begin + rank_count <= dcp_size
+ * out_o       device, [rank_count, batch, num_q_heads, head_dim_v] float32
+ * out_lse     device, [rank_count, batch, num_q_heads] float32 (natural log)
+ * workspace   device, >= the size query's bytes (may be NULL if that is 0)
+ * Errors: DCP_ERR_INVALID_ARG (sizes, relations, NULL pointers,
+ * num_q_heads % num_kv_heads != 0, head_dim_v > head_dim_k with v == NULL,
+ * fp8 without scales), DCP_ERR_UNSUPPORTED, DCP_ERR_WORKSPACE, DCP_ERR_HIP.
+ */
+int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                            const dcp_kv_cache_t* kv, const int32_t* block_table,
+                            int64_t block_table_stride, int32_t max_vblocks,
+                            const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
+                            int32_t rank_count, float softmax_scale, int32_t algo,
+                            float* out_o, float* out_lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * dcp_lse_merge - combine per-rank partials into exact attention, applying an
+ * attention sink once.
+ *
+ * Source: "Decode Context Parallel (DCP)", section "Decode" (partial outputs
+ * and LSE values are combined across the DCP group); "DeepSeek V4.1 context
+ * parallelism", section "Decode computation" (the attention sink is applied
+ * once when the partial outputs are merged by log-sum-exp).
+ *
+ * For each (b, h), over parts r with LSE_r = part_lse[(r*batch + b)*num_heads + h]:
+ *   M   = max(max_r LSE_r, sink[h])          (sink term only if sink != NULL)
+ *   Z   = sum_r exp(LSE_r - M) + exp(sink[h] - M)
+ *   LSE = M + ln Z
+ *   O   = sum_r exp(LSE_r - LSE) * part_o[r, b, h, :]
+ * Parts with LSE_r = -inf contribute nothing; when every term is -inf, O = 0
+ * and LSE = -inf. The sink is a logit in the units of the scaled scores with
+ * a zero value vector; the returned LSE includes it.
+ *
+ * part_o    device, [num_parts, batch, num_heads, head_dim_v] float32
+ * part_lse  device, [num_parts, batch, num_heads] float32
+ * num_parts 1..64; batch >= 0; num_heads >= 1; head_dim_v 1..1024
+ * sink      device, [num_heads] float32, or NULL
+ * out_dtype DCP_F32 or DCP_BF16 (round to nearest even)
+ * out_o     device, [batch, num_heads, head_dim_v]
+ * out_lse   device, [batch, num_heads] float32, or NULL
+ * Errors: DCP_ERR_INVALID_ARG, DCP_ERR_UNSUPPORTED, DCP_ERR_HIP.
+ */
+int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts, int32_t batch,
+                  int32_t num_heads, int32_t head_dim_v, const float* sink, int32_t out_dtype,
+                  void* out_o, float* out_lse, void* stream);
+
+/*
+ * Measurement hook for benchmarks.
+ *
+ * dcp_profile_enable(1) makes every following dcp_partial_decode_attn call
+ * made by this host thread record a pair of HIP events on its stream, right
+ * before and right after its main attention kernel (the planner and the split
+ * combine are outside the pair). dcp_profile_collect waits for the recorded
+ * events, returns the summed elapsed milliseconds and the number of calls
+ * since the last collect (or enable), and starts a new count.
+ * dcp_profile_enable(0) stops recording. The events are created by the
+ * library on first use and reused; nothing else changes in the calls.
+ * Errors: DCP_ERR_INVALID_ARG (NULL output), DCP_ERR_HIP.
+ */
+int dcp_profile_enable(int on);
+int dcp_profile_collect(double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H */

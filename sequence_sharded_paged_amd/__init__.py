@@ -1,0 +1,15 @@
+"""MI355X-native Decode Context Parallel (DCP) decode attention.
+
+The compute lives in libdcp (HIP, gfx950), reached through the C ABI in
+include/dcp.h; ``native`` is the thin ctypes binding with the same function
+names, ``cache`` holds the per-rank paged KV pools in the layouts the kernels
+read. Importing this package does not load the library; the first call does,
+and raises if it has not been built.
+"""
+
+from .native import (  # noqa: F401
+    DCP_ALGO_AUTO, DCP_ALGO_FAST, DCP_ALGO_GENERIC, DCP_BF16, DCP_F32, DCP_FP8_E4M3, DcpError, KvCache,
+    dcp_abi_version, dcp_local_seq_lens, dcp_lse_merge, dcp_partial_decode_attn,
+    dcp_partial_decode_attn_workspace_size, dcp_slot_mapping, dcp_status_string,
+)
+from .cache import PagedKVCache  # noqa: F401

@@ -1,0 +1,250 @@
+// C ABI entry points of libdcp: host-side validation, kernel selection and
+// launch. The operations and their sources are documented in include/dcp.h.
+#include <atomic>
+#include <cmath>
+#include <utility>
+#include <vector>
+
+#include "common.h"
+
+namespace dcp {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  static std::atomic<bool> init{false};
+  if (!init.load()) {
+    for (auto& c : cache) c.store(0);
+    init.store(true);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev].load() > 0) return cache[dev].load();
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus);
+  return cus;
+}
+
+static int check_layout_args(int32_t block_size, int32_t dcp_size, int32_t interleave) {
+  if (block_size < 1 || dcp_size < 1 || interleave < 1) return DCP_ERR_INVALID_ARG;
+  if (block_size % interleave != 0) return DCP_ERR_INVALID_ARG;
+  return DCP_OK;
+}
+
+static bool valid_dtype(int32_t t) { return t == DCP_F32 || t == DCP_BF16 || t == DCP_FP8_E4M3; }
+
+// Validation shared by the size query and the launch. Fills p (except the
+// output, workspace and stream fields) and picks the kernel family.
+static int validate_attn(int32_t batch, int32_t num_q_heads, int32_t q_dtype, const dcp_kv_cache_t* kv,
+                         int32_t rank_count, int32_t algo, AttnParams& p, AttnKernel& kernel) {
+  if (!kv) return DCP_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads < 1 || rank_count < 1) return DCP_ERR_INVALID_ARG;
+  if (q_dtype != DCP_F32 && q_dtype != DCP_BF16) return DCP_ERR_UNSUPPORTED;
+  if (!valid_dtype(kv->dtype)) return DCP_ERR_UNSUPPORTED;
+  if (kv->num_kv_heads < 1 || num_q_heads % kv->num_kv_heads != 0) return DCP_ERR_INVALID_ARG;
+  if (kv->block_size < 1 || kv->num_blocks < 1) return DCP_ERR_INVALID_ARG;
+  if (kv->head_dim_k < 1 || kv->head_dim_v < 1) return DCP_ERR_INVALID_ARG;
+  if (!kv->v && kv->head_dim_v > kv->head_dim_k) return DCP_ERR_INVALID_ARG;
+  if (kv->head_dim_k > 1024 || kv->head_dim_v > 1024) return DCP_ERR_UNSUPPORTED;
+  if (kv->dtype == DCP_FP8_E4M3 && (!kv->k_scale || !kv->v_scale)) return DCP_ERR_INVALID_ARG;
+  if (algo != DCP_ALGO_AUTO && algo != DCP_ALGO_GENERIC && algo != DCP_ALGO_FAST) return DCP_ERR_INVALID_ARG;
+  p.q_dtype = q_dtype;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.group = num_q_heads / kv->num_kv_heads;
+  p.kv = *kv;
+  p.rank_count = rank_count;
+  if (algo == DCP_ALGO_GENERIC) {
+    kernel = AttnKernel::Generic;
+  } else if (gqa_supported(p)) {
+    kernel = AttnKernel::GqaMfma;
+  } else if (mla_supported(p)) {
+    kernel = AttnKernel::MlaMfma;
+  } else if (algo == DCP_ALGO_FAST) {
+    return DCP_ERR_UNSUPPORTED;
+  } else {
+    kernel = AttnKernel::Generic;
+  }
+  return DCP_OK;
+}
+
+static size_t workspace_for(const AttnParams& p, AttnKernel k) {
+  switch (k) {
+    case AttnKernel::GqaMfma: return gqa_workspace_bytes(p);
+    case AttnKernel::MlaMfma: return mla_workspace_bytes(p);
+    default: return generic_workspace_bytes(p);
+  }
+}
+
+// Kernel timing for benchmarks (dcp_profile_enable / dcp_profile_collect):
+// per host thread, a growing pool of event pairs, one pair per profiled call.
+struct ProfileState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+  size_t used = 0;
+  int device = -1;
+};
+static thread_local ProfileState g_prof;
+
+static void profile_release() {
+  for (auto& e : g_prof.events) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  g_prof.events.clear();
+  g_prof.used = 0;
+}
+
+// Event pair for the next profiled call, or {nullptr, nullptr}.
+static std::pair<hipEvent_t, hipEvent_t> profile_next() {
+  if (!g_prof.on) return {nullptr, nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return {nullptr, nullptr};
+  if (dev != g_prof.device) {
+    profile_release();
+    g_prof.device = dev;
+  }
+  if (g_prof.used == g_prof.events.size()) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return {nullptr, nullptr};
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return {nullptr, nullptr};
+    }
+    g_prof.events.emplace_back(a, b);
+  }
+  return g_prof.events[g_prof.used++];
+}
+
+}  // namespace dcp
+
+using namespace dcp;
+
+extern "C" {
+
+int dcp_abi_version(void) { return 1; }
+
+const char* dcp_status_string(int status) {
+  switch (status) {
+    case DCP_OK: return "ok";
+    case DCP_ERR_INVALID_ARG: return "invalid argument";
+    case DCP_ERR_UNSUPPORTED: return "unsupported dtype, geometry or layout";
+    case DCP_ERR_WORKSPACE: return "workspace too small";
+    case DCP_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int dcp_local_seq_lens(const int32_t* seq_lens, int32_t num_reqs, int32_t block_size, int32_t dcp_size,
+                       int32_t interleave, int32_t* local_lens, void* stream) {
+  if (int st = check_layout_args(block_size, dcp_size, interleave)) return st;
+  if (num_reqs < 0) return DCP_ERR_INVALID_ARG;
+  if (num_reqs == 0) return DCP_OK;
+  if (!seq_lens || !local_lens) return DCP_ERR_INVALID_ARG;
+  return launch_local_seq_lens(seq_lens, num_reqs, dcp_size, interleave, local_lens,
+                               static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
+int dcp_slot_mapping(const int64_t* positions, const int32_t* req_indices, int64_t num_tokens,
+                     const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
+                     int32_t max_vblocks, int32_t block_size, int32_t dcp_size, int32_t interleave,
+                     int64_t* slots, void* stream) {
+  if (int st = check_layout_args(block_size, dcp_size, interleave)) return st;
+  if (num_tokens < 0 || num_reqs < 0 || max_vblocks < 0 || block_table_stride < max_vblocks)
+    return DCP_ERR_INVALID_ARG;
+  if (num_tokens == 0) return DCP_OK;
+  if (!positions || !req_indices || !slots) return DCP_ERR_INVALID_ARG;
+  if (num_reqs > 0 && max_vblocks > 0 && !block_table) return DCP_ERR_INVALID_ARG;
+  if (num_tokens > (int64_t(1) << 40)) return DCP_ERR_INVALID_ARG;
+  return launch_slot_mapping(positions, req_indices, num_tokens, block_table, num_reqs, block_table_stride,
+                             max_vblocks, block_size, dcp_size, interleave, slots,
+                             static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
+size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
+                                              const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo,
+                                              int* status) {
+  AttnParams p{};
+  AttnKernel k = AttnKernel::Generic;
+  const int st = validate_attn(batch, num_q_heads, q_dtype, kv, rank_count, algo, p, k);
+  if (status) *status = st;
+  if (st != DCP_OK) return 0;
+  return workspace_for(p, k);
+}
+
+int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                            const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
+                            int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
+                            int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  AttnParams p{};
+  AttnKernel k = AttnKernel::Generic;
+  if (int st = validate_attn(batch, num_q_heads, q_dtype, kv, rank_count, algo, p, k)) return st;
+  if (dcp_size < 1 || rank_begin < 0 || rank_begin + rank_count > dcp_size) return DCP_ERR_INVALID_ARG;
+  if (max_vblocks < 0 || block_table_stride < max_vblocks) return DCP_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return DCP_ERR_INVALID_ARG;
+  if (batch == 0) return DCP_OK;
+  if (!q || !kv->k || !local_lens || !out_o || !out_lse) return DCP_ERR_INVALID_ARG;
+  if (max_vblocks > 0 && !block_table) return DCP_ERR_INVALID_ARG;
+  const size_t need = workspace_for(p, k);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return DCP_ERR_WORKSPACE;
+  p.q = q;
+  p.block_table = block_table;
+  p.bt_stride = block_table_stride;
+  p.max_vblocks = max_vblocks;
+  p.local_lens = local_lens;
+  p.dcp_size = dcp_size;
+  p.rank_begin = rank_begin;
+  p.softmax_scale = softmax_scale;
+  p.out_o = out_o;
+  p.out_lse = out_lse;
+  p.workspace = workspace;
+  p.workspace_bytes = workspace_bytes;
+  p.stream = static_cast<hipStream_t>(stream);
+  const auto ev = profile_next();
+  p.ev_begin = ev.first;
+  p.ev_end = ev.second;
+  hipError_t e;
+  switch (k) {
+    case AttnKernel::GqaMfma: e = launch_gqa_attn(p); break;
+    case AttnKernel::MlaMfma: e = launch_mla_attn(p); break;
+    default: e = launch_generic_attn(p); break;
+  }
+  return e == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
+int dcp_profile_enable(int on) {
+  g_prof.on = on != 0;
+  g_prof.used = 0;
+  return DCP_OK;
+}
+
+int dcp_profile_collect(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return DCP_ERR_INVALID_ARG;
+  double sum = 0.0;
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.events[i].second) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.events[i].first, g_prof.events[i].second) != hipSuccess)
+      return DCP_ERR_HIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int32_t>(g_prof.used);
+  g_prof.used = 0;
+  return DCP_OK;
+}
+
+int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts, int32_t batch, int32_t num_heads,
+                  int32_t head_dim_v, const float* sink, int32_t out_dtype, void* out_o, float* out_lse,
+                  void* stream) {
+  if (num_parts < 1 || num_parts > 64 || batch < 0 || num_heads < 1 || head_dim_v < 1 || head_dim_v > 4096)
+    return DCP_ERR_INVALID_ARG;
+  if (out_dtype != DCP_F32 && out_dtype != DCP_BF16) return DCP_ERR_UNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!part_o || !part_lse || !out_o) return DCP_ERR_INVALID_ARG;
+  return launch_lse_merge(part_o, part_lse, num_parts, batch, num_heads, head_dim_v, sink, out_dtype, out_o,
+                          out_lse, static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
+}  // extern "C"

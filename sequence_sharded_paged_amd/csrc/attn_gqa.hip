@@ -1,0 +1,462 @@
+// GQA per-rank partial decode attention on MFMA (bf16 or fp8-e4m3 KV, head
+// dim 128, up to 16 query heads per KV head).
+//
+// Source: "Decode Context Parallel (DCP)" (vLLM Ascend design doc), section
+// "Decode" (attention of the gathered query heads against the local KV shard,
+// partial output and LSE out); "Efficient Decode Context Parallelism with vLLM
+// for Long Context Workloads", section 5.4 (the query heads of a group share
+// one KV head).
+//
+// Work split ("stream-K"): a unit is (rank, request, KV head); its local
+// tokens are cut into tiles of TOK tokens; the tiles of all units, in unit
+// order, are dealt out in equal contiguous ranges to persistent wavefronts.
+// A wavefront that covers a whole unit writes the unit's final (O, LSE); a
+// unit cut between wavefronts leaves up to one unnormalised partial per side
+// in the workspace and a combine kernel merges them by log-sum-exp. A planner
+// kernel builds the tile prefix over units on the device, so the grid depends
+// only on the device, never on the lengths (graph-safe).
+//
+// Per wavefront and tile, with lane l = 16*qd + n (n = l % 16, qd = l / 16):
+//   scores  S^T[token, head] = K[token, :] . Q[head, :]   (MFMA 16x16x32 bf16,
+//           A = K rows loaded straight from HBM in operand layout, B = Q^T
+//           held in registers, head columns >= group are zero)
+//   softmax online, per head column: running max and sums; the weights are
+//           rounded to bf16 for the value product and the same rounded values
+//           form the normalising sum (O is an exact convex combination of the
+//           values), while an fp32 sum of the unrounded weights gives the LSE
+//   values  O^T[dim, head] += V^T[dim, token] . P^T[token, head] (A = V^T,
+//           read straight from HBM because V is stored transposed inside a
+//           block, [block, head, dim, token]; B = P^T from the score registers)
+// The token order inside a tile is permuted so that the score accumulator of
+// lane l already holds exactly the weights that lane must feed to the value
+// product: no LDS, no shuffles besides the max/sum reductions. fp8 codes are
+// widened to bf16 in registers (exact) and the per-head scales are applied to
+// the scores and to the output, outside the dot products.
+#include "common.h"
+
+namespace dcp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGqaDim = 128;
+constexpr int kGqaMaxWorkers = 8192;
+constexpr int kGqaWavesPerBlock = 4;
+constexpr int kPlanThreads = 1024;
+constexpr int kPartExtra = 3;  // per partial head row: O[128], m (log2 units), rounded sum, fp32 sum
+
+template <bool kFp8>
+struct GqaTile {
+  static constexpr int TOK = kFp8 ? 64 : 32;  // tokens per tile
+  static constexpr int NT = TOK / 16;         // score row tiles (16 tokens each)
+  static constexpr int RUN = TOK / 4;         // consecutive tokens per lane group
+  static constexpr int KS = TOK / 32;         // value-product k-steps
+};
+
+// 8 fp8 codes (two dwords) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// Zero bytes [keep, 16) of a 16-byte vector.
+__device__ __forceinline__ u32x4_t keep_bytes(u32x4_t v, int keep) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = keep - 4 * i;
+    const uint32_t m = k >= 4 ? 0xffffffffu : (k <= 0 ? 0u : (0xffffffffu >> (32 - 8 * k)));
+    v[i] &= m;
+  }
+  return v;
+}
+
+struct GqaWs {
+  int64_t* prefix;     // [U + 1] tile prefix over units
+  int32_t* wunit;      // [kGqaMaxWorkers] unit holding each worker's first tile
+  float* part;         // [kGqaMaxWorkers][2][group][Dv + kPartExtra]
+};
+
+__host__ __device__ inline GqaWs gqa_ws(void* base, int64_t units) {
+  GqaWs w;
+  char* p = static_cast<char*>(base);
+  w.prefix = reinterpret_cast<int64_t*>(p);
+  p += align_up(static_cast<size_t>(units + 1) * sizeof(int64_t), 256);
+  w.wunit = reinterpret_cast<int32_t*>(p);
+  p += align_up(static_cast<size_t>(kGqaMaxWorkers) * sizeof(int32_t), 256);
+  w.part = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Planner: tile prefix over units and each worker's first unit (one block).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPlanThreads) gqa_plan_kernel(AttnParams p, int tok, int workers) {
+  __shared__ int64_t scan[kPlanThreads];
+  __shared__ int64_t total_s;
+  const int Hkv = p.kv.num_kv_heads;
+  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
+  GqaWs ws = gqa_ws(p.workspace, U);
+  const int tid = threadIdx.x;
+  const int64_t chunk = (U + kPlanThreads - 1) / kPlanThreads;
+  const int64_t u0 = min(U, tid * chunk), u1 = min(U, u0 + chunk);
+  auto tiles = [&](int64_t u) -> int64_t {
+    const int64_t rb = u / Hkv;  // r * batch + b
+    const int b = static_cast<int>(rb % p.batch), r = static_cast<int>(rb / p.batch);
+    const int64_t n = max(p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r], 0);
+    return (n + tok - 1) / tok;
+  };
+  int64_t s = 0;
+  for (int64_t u = u0; u < u1; ++u) s += tiles(u);
+  scan[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {  // Hillis-Steele inclusive scan
+    const int64_t v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int64_t run = scan[tid] - s;  // exclusive prefix
+  for (int64_t u = u0; u < u1; ++u) {
+    ws.prefix[u] = run;
+    run += tiles(u);
+  }
+  if (tid == kPlanThreads - 1) {
+    ws.prefix[U] = scan[tid];
+    total_s = scan[tid];
+  }
+  __syncthreads();
+  const int64_t T = total_s;
+  if (T == 0) return;
+  const int64_t tpw = (T + workers - 1) / workers;
+  run = scan[tid] - s;
+  for (int64_t u = u0; u < u1; ++u) {
+    const int64_t nxt = run + tiles(u);
+    // workers whose first tile lies in [run, nxt)
+    for (int64_t w = (run + tpw - 1) / tpw; w < (nxt + tpw - 1) / tpw && w < workers; ++w)
+      ws.wunit[w] = static_cast<int32_t>(u);
+    run = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel: one persistent wavefront per worker.
+// ---------------------------------------------------------------------------
+template <bool kFp8>
+__global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnParams p, int workers) {
+  using C = GqaTile<kFp8>;
+  constexpr int TOK = C::TOK, NT = C::NT, RUN = C::RUN;
+  const int lane = threadIdx.x & 63;
+  const int worker = blockIdx.x * kGqaWavesPerBlock + (threadIdx.x >> 6);
+  const int n = lane & 15, qd = lane >> 4;
+  const int Hkv = p.kv.num_kv_heads, G = p.group;
+  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
+  GqaWs ws = gqa_ws(p.workspace, U);
+  const int64_t T = ws.prefix[U];
+  if (worker >= workers || T == 0) return;
+  const int64_t tpw = (T + workers - 1) / workers;
+  const int64_t wstart = worker * tpw;
+  if (wstart >= T) return;
+  const int64_t wend = min(T, wstart + tpw);
+
+  const int bs = p.kv.block_size;
+  const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks2 = p.kv.k_stride[2], ks3 = p.kv.k_stride[3];
+  const int64_t vs0 = p.kv.v_stride[0], vs1 = p.kv.v_stride[1], vs2 = p.kv.v_stride[2], vs4 = p.kv.v_stride[4];
+  constexpr int EB = kFp8 ? 1 : 2;
+  const char* kbase = static_cast<const char*>(p.kv.k);
+  const char* vbase = static_cast<const char*>(p.kv.v);
+
+  int64_t u = ws.wunit[worker];
+  int64_t tile = wstart;
+  while (tile < wend) {
+    const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
+    if (uend <= tile) { ++u; continue; }
+    const int64_t t_lo = tile - ubeg, t_hi = min(wend, uend) - ubeg;  // unit-local tile range
+    const int h = static_cast<int>(u % Hkv);
+    const int64_t rb = u / Hkv;
+    const int b = static_cast<int>(rb % p.batch), r = static_cast<int>(rb / p.batch);
+    const int len = p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r];
+    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+    const char* kh = kbase + (r * ks0 + h * ks2) * EB;
+    const char* vh = vbase + (r * vs0 + h * vs2) * EB;
+    const float kscale = kFp8 ? p.kv.k_scale[h] : 1.f;
+    const float vscale = kFp8 ? p.kv.v_scale[h] : 1.f;
+    const float c2 = p.softmax_scale * kscale * DCP_LOG2E;
+
+    // Q^T operand for the 4 k-steps over the 128 dims (zero for head >= G).
+    bf16x8_t qop[4];
+    {
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
+                             (static_cast<int64_t>(b) * p.num_q_heads + h * G + n) * kGqaDim;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d0 = kFp8 ? (64 * (k >> 1) + 16 * qd + 8 * (k & 1)) : (32 * k + 8 * qd);
+        u32x4_t raw = {0u, 0u, 0u, 0u};
+        if (n < G) raw = ldg16(qrow + d0);
+        qop[k] = __builtin_bit_cast(bf16x8_t, raw);
+      }
+    }
+
+    f32x4_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // l_run sums the bf16-rounded weights that enter the value product (so O
+    // is an exact convex combination of the values); e_run sums the fp32
+    // weights and gives the LSE.
+    float m_run = -INFINITY, l_run = 0.f, e_run = 0.f;
+
+    for (int64_t t = t_lo; t < t_hi; ++t) {
+      const int t0 = static_cast<int>(t * TOK);
+      // ---- loads: K rows in operand layout, V^T runs --------------------
+      u32x4_t kraw[NT][kFp8 ? 2 : 4];
+#pragma unroll
+      for (int ut = 0; ut < NT; ++ut) {
+        const int tok = t0 + RUN * (n >> 2) + 4 * ut + (n & 3);
+        if (tok < len) {
+          const int64_t phys = bt[tok / bs];
+          const char* row = kh + (phys * ks1 + static_cast<int64_t>(tok % bs) * ks3) * EB;
+#pragma unroll
+          for (int j = 0; j < (kFp8 ? 2 : 4); ++j)
+            kraw[ut][j] = ldg16(row + (kFp8 ? (16 * qd + 64 * j) : (16 * qd + 64 * j)));
+        } else {
+#pragma unroll
+          for (int j = 0; j < (kFp8 ? 2 : 4); ++j) kraw[ut][j] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+      u32x4_t vraw[8];
+      {
+        const int tok = t0 + RUN * qd;
+        if (tok < len) {
+          const int64_t phys = bt[tok / bs];
+          const char* run = vh + (phys * vs1 + static_cast<int64_t>(tok % bs)) * EB;
+          const int keep = (len - tok) * EB;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            u32x4_t v = ldg16(run + static_cast<int64_t>(16 * nt + n) * vs4 * EB);
+            vraw[nt] = keep < 16 ? keep_bytes(v, keep) : v;
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) vraw[nt] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+      // ---- scores ---------------------------------------------------------
+      f32x4_t s[NT];
+#pragma unroll
+      for (int ut = 0; ut < NT; ++ut) {
+        s[ut] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          bf16x8_t a;
+          if constexpr (kFp8) {
+            const u32x4_t& w = kraw[ut][k >> 1];
+            a = (k & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+          } else {
+            a = __builtin_bit_cast(bf16x8_t, kraw[ut][k]);
+          }
+          s[ut] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[k], s[ut], 0, 0, 0);
+        }
+      }
+      // ---- online softmax (log2 domain) ----------------------------------
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int ut = 0; ut < NT; ++ut)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t0 + RUN * qd + 4 * ut + i;
+          const float x = tok < len ? s[ut][i] * c2 : -INFINITY;
+          s[ut][i] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_run, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      m_run = m_new;
+      __bf16 pb[NT][4];
+      float psum = 0.f, esum = 0.f;
+#pragma unroll
+      for (int ut = 0; ut < NT; ++ut)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2f(s[ut][i] - m_use);
+          const __bf16 eb = static_cast<__bf16>(e);
+          pb[ut][i] = eb;
+          psum += static_cast<float>(eb);
+          esum += e;
+        }
+      l_run = l_run * alpha + psum;
+      e_run = e_run * alpha + esum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      // ---- values ---------------------------------------------------------
+#pragma unroll
+      for (int ksx = 0; ksx < C::KS; ++ksx) {
+        const bf16x8_t pop = {pb[2 * ksx][0], pb[2 * ksx][1], pb[2 * ksx][2], pb[2 * ksx][3],
+                              pb[2 * ksx + 1][0], pb[2 * ksx + 1][1], pb[2 * ksx + 1][2], pb[2 * ksx + 1][3]};
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          bf16x8_t a;
+          if constexpr (kFp8) {
+            a = ksx ? fp8x8_to_bf16x8(vraw[nt][2], vraw[nt][3]) : fp8x8_to_bf16x8(vraw[nt][0], vraw[nt][1]);
+          } else {
+            a = __builtin_bit_cast(bf16x8_t, vraw[nt]);
+          }
+          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, o[nt], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- piece end: full unit -> final output, else partial --------------
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    float e_tot = e_run + __shfl_xor(e_run, 16, 64);
+    e_tot += __shfl_xor(e_tot, 32, 64);
+    const bool whole = (t_lo == 0) && (t_hi == uend - ubeg);
+    if (whole) {
+      const float inv = vscale / l_tot;
+      if (n < G) {
+        const int64_t row = (rb * p.num_q_heads + static_cast<int64_t>(h) * G + n);
+        float* dst = p.out_o + row * kGqaDim;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          f32x4_t v = o[nt] * inv;
+          *reinterpret_cast<f32x4_t*>(dst + 16 * nt + 4 * qd) = v;
+        }
+        if (qd == 0) p.out_lse[row] = (m_run + __log2f(e_tot)) * DCP_LN2;
+      }
+    } else {
+      const int which = (t_lo == 0) ? 1 : 0;  // 0: unit began before this worker
+      float* dst = ws.part + ((static_cast<int64_t>(worker) * 2 + which) * G) * (kGqaDim + kPartExtra);
+      if (n < G) {
+        float* hrow = dst + static_cast<int64_t>(n) * (kGqaDim + kPartExtra);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          f32x4_t v = o[nt] * vscale;
+          *reinterpret_cast<f32x4_t*>(hrow + 16 * nt + 4 * qd) = v;
+        }
+        if (qd == 0) {
+          hrow[kGqaDim] = m_run;
+          hrow[kGqaDim + 1] = l_tot;
+          hrow[kGqaDim + 2] = e_tot;
+        }
+      }
+    }
+    tile = ubeg + t_hi;
+    ++u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: merge the pieces of units cut between workers; zero empty units.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(128) gqa_combine_kernel(AttnParams p, int workers) {
+  const int Hkv = p.kv.num_kv_heads, G = p.group;
+  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
+  const int64_t u = blockIdx.x;
+  GqaWs ws = gqa_ws(p.workspace, U);
+  const int64_t T = ws.prefix[U];
+  const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
+  const int h = static_cast<int>(u % Hkv);
+  const int64_t rb = u / Hkv;
+  const int d = threadIdx.x;
+  if (ubeg == uend) {  // empty shard: O = 0, LSE = -inf
+    for (int g = 0; g < G; ++g) {
+      const int64_t row = rb * p.num_q_heads + static_cast<int64_t>(h) * G + g;
+      p.out_o[row * kGqaDim + d] = 0.f;
+      if (d == 0) p.out_lse[row] = -INFINITY;
+    }
+    return;
+  }
+  const int64_t tpw = (T + workers - 1) / workers;
+  const int64_t wa = ubeg / tpw, wb = (uend - 1) / tpw;
+  if (wa == wb) return;  // written whole by one worker
+  for (int g = 0; g < G; ++g) {
+    float mx = -INFINITY;
+    for (int64_t w = wa; w <= wb; ++w) {
+      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * G + g) * (kGqaDim + kPartExtra);
+      mx = fmaxf(mx, hrow[kGqaDim]);
+    }
+    float acc = 0.f, lsum = 0.f, esum = 0.f;
+    for (int64_t w = wa; w <= wb; ++w) {
+      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * G + g) * (kGqaDim + kPartExtra);
+      const float sc = exp2f(hrow[kGqaDim] - mx);
+      acc += sc * hrow[d];
+      lsum += sc * hrow[kGqaDim + 1];
+      esum += sc * hrow[kGqaDim + 2];
+    }
+    const int64_t row = rb * p.num_q_heads + static_cast<int64_t>(h) * G + g;
+    p.out_o[row * kGqaDim + d] = acc / lsum;
+    if (d == 0) p.out_lse[row] = (mx + __log2f(esum)) * DCP_LN2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+bool gqa_supported(const AttnParams& p) {
+  const dcp_kv_cache_t& kv = p.kv;
+  if (p.q_dtype != DCP_BF16) return false;
+  if (kv.dtype != DCP_BF16 && kv.dtype != DCP_FP8_E4M3) return false;
+  if (kv.head_dim_k != kGqaDim || kv.head_dim_v != kGqaDim || !kv.v) return false;
+  if (p.group > 16) return false;
+  if (kv.block_size % 16 != 0) return false;
+  if (kv.k_stride[4] != 1 || kv.v_stride[3] != 1) return false;
+  const int eb = kv.dtype == DCP_BF16 ? 2 : 1;
+  // 16-byte alignment of every row / run the kernel loads
+  for (int i = 0; i < 4; ++i)
+    if ((kv.k_stride[i] * eb) % 16 != 0) return false;
+  for (int i : {0, 1, 2, 4})
+    if ((kv.v_stride[i] * eb) % 16 != 0) return false;
+  if (reinterpret_cast<uintptr_t>(kv.k) % 16 || reinterpret_cast<uintptr_t>(kv.v) % 16) return false;
+  return true;
+}
+
+size_t gqa_workspace_bytes(const AttnParams& p) {
+  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
+  size_t b = align_up(static_cast<size_t>(U + 1) * sizeof(int64_t), 256);
+  b += align_up(static_cast<size_t>(kGqaMaxWorkers) * sizeof(int32_t), 256);
+  b += static_cast<size_t>(kGqaMaxWorkers) * 2 * p.group * (kGqaDim + kPartExtra) * sizeof(float);
+  return b;
+}
+
+template <bool kFp8>
+static int gqa_workers() {
+  static int cached[2] = {0, 0};
+  int& c = cached[kFp8 ? 1 : 0];
+  if (c == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_attn_kernel<kFp8>, 64 * kGqaWavesPerBlock, 0) !=
+            hipSuccess || per_cu < 1)
+      per_cu = 2;
+    c = min(kGqaMaxWorkers, device_cu_count() * per_cu * kGqaWavesPerBlock);
+  }
+  return c;
+}
+
+hipError_t launch_gqa_attn(const AttnParams& p) {
+  const bool fp8 = p.kv.dtype == DCP_FP8_E4M3;
+  const int workers = fp8 ? gqa_workers<true>() : gqa_workers<false>();
+  const int tok = fp8 ? GqaTile<true>::TOK : GqaTile<false>::TOK;
+  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
+  hipLaunchKernelGGL(gqa_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, tok, workers);
+  const dim3 grid((workers + kGqaWavesPerBlock - 1) / kGqaWavesPerBlock);
+  if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
+  if (fp8)
+    hipLaunchKernelGGL(gqa_attn_kernel<true>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
+  else
+    hipLaunchKernelGGL(gqa_attn_kernel<false>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
+  if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
+  hipLaunchKernelGGL(gqa_combine_kernel, dim3(static_cast<unsigned>(U)), dim3(kGqaDim), 0, p.stream, p, workers);
+  return hipGetLastError();
+}
+
+}  // namespace dcp

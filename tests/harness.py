@@ -1,0 +1,166 @@
+"""Shared test plumbing: device inputs for the HIP path, oracle evaluation on
+the host, and the parity checks (tolerances from the project's acceptance
+bar: max-abs 1e-5 for fp32 and 2e-2 for bf16/fp8 inputs, plus a per-row
+relative bound and an LSE bound so that long rows, whose outputs are small,
+cannot pass vacuously)."""
+
+import numpy as np
+import torch
+
+import sequence_sharded_paged_amd as dcp
+from oracle import attention as oatt
+from oracle import formats as ofmt
+from oracle import layout as olay
+from workloads.generate import stored_numpy, stored_format
+
+TOL = {
+    "fp32": dict(max_abs=1e-5, row_rel=1e-4, lse=1e-5),
+    "bf16": dict(max_abs=2e-2, row_rel=1e-2, lse=1e-3),
+    "fp8_e4m3": dict(max_abs=2e-2, row_rel=1e-2, lse=1e-3),
+}
+OUT_BF16_EXTRA = 2.0 ** -8   # relative rounding of a bf16 output element
+
+
+class DeviceInputs:
+    """Everything the HIP path reads, built from a generated ``Case``."""
+
+    def __init__(self, case, device="cuda", dcp_size=None, interleave=None, v_layout="dim_major",
+                 fill="nan"):
+        w = case.workload
+        self.case, self.w = case, w
+        self.D = dcp_size or w.dcp_size
+        self.I = interleave or w.interleave
+        self.bs = w.block_size
+        lens = case.seq_lens
+        if dcp_size is not None or interleave is not None:
+            span = self.bs * self.D
+            nvb = [(int(L) + span - 1) // span for L in lens]
+            rng = np.random.default_rng(1234)
+            nblk = max(1, sum(nvb))
+            perm = rng.permutation(nblk).astype(np.int32)
+            table = np.full((len(lens), max(nvb + [1])), -1, dtype=np.int32)
+            pos = 0
+            for b, n in enumerate(nvb):
+                table[b, :n] = perm[pos:pos + n]
+                pos += n
+        else:
+            table, nblk = case.block_table, case.num_blocks
+        self.block_table_np = table
+        self.block_table = torch.from_numpy(table).to(device)
+        self.seq_lens = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.local_lens = dcp.dcp_local_seq_lens(self.seq_lens, self.bs, self.D, self.I)
+        self.q = case.q.to(device)
+        kv_dtype = case.k[0].dtype
+        self.cache = dcp.PagedKVCache(self.D, nblk, self.bs, w.num_kv_heads, w.head_dim_k, w.head_dim_v,
+                                      kv_dtype, mla=w.mla, device=device, v_layout=v_layout,
+                                      k_scale=case.k_scale, v_scale=case.v_scale, fill=fill)
+        for b in range(case.batch):
+            L = int(lens[b])
+            if L == 0:
+                continue
+            pos = torch.arange(L, dtype=torch.int64, device=device)
+            req = torch.full((L,), b, dtype=torch.int32, device=device)
+            slots = dcp.dcp_slot_mapping(pos, req, self.block_table, self.bs, self.D, self.I)
+            self.cache.write(slots, case.k[b].to(device), None if case.v is None else case.v[b].to(device))
+        self.sink = None if case.sink is None else torch.from_numpy(case.sink).to(device)
+        torch.cuda.synchronize()
+
+    def prepare(self, algo=dcp.DCP_ALGO_AUTO, rank_begin=0, rank_count=None, out_dtype=None):
+        """Allocate workspace and outputs once (NaN-filled so unwritten
+        entries show up); ``step`` then launches without allocating."""
+        w = self.w
+        R = self.D - rank_begin if rank_count is None else rank_count
+        B, Hq = self.q.shape[0], self.q.shape[1]
+        dev = self.q.device
+        self.algo, self.rank_begin, self.rank_count = algo, rank_begin, R
+        self.kv = self.cache.descriptor(rank_begin)
+        ws_bytes = dcp.dcp_partial_decode_attn_workspace_size(B, Hq, dcp.native.TORCH_TO_DCP[self.q.dtype],
+                                                              self.kv, R, algo)
+        self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.po = torch.full((R, B, Hq, w.head_dim_v), float("nan"), dtype=torch.float32, device=dev)
+        self.pl = torch.full((R, B, Hq), float("nan"), dtype=torch.float32, device=dev)
+        od = {"bf16": torch.bfloat16, "fp32": torch.float32}[out_dtype or w.out_format]
+        self.o = torch.full((B, Hq, w.head_dim_v), float("nan"), dtype=od, device=dev)
+        self.lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+        return self
+
+    def partial(self):
+        dcp.dcp_partial_decode_attn(self.q, self.kv, self.block_table, self.local_lens, self.D, self.rank_begin,
+                                    self.rank_count, self.w.softmax_scale, self.po, self.pl, self.ws,
+                                    algo=self.algo)
+
+    def merge(self):
+        dcp.dcp_lse_merge(self.po, self.pl, sink=self.sink, out_o=self.o, out_lse=self.lse)
+
+    def step(self):
+        """One decode step: every rank's partial attention, then the merge."""
+        self.partial()
+        self.merge()
+
+    def run(self, algo=dcp.DCP_ALGO_AUTO, rank_begin=0, rank_count=None, out_dtype=None):
+        self.prepare(algo, rank_begin, rank_count, out_dtype)
+        self.step()
+        torch.cuda.synchronize()
+        return self.po, self.pl, self.o, self.lse
+
+
+def oracle_request(case, b, dcp_size=None, interleave=None, with_partials=True):
+    """Float64 oracle for request b: full attention (with the sink) and the
+    per-rank partials over the brute-force ownership."""
+    w = case.workload
+    D = dcp_size or w.dcp_size
+    I = interleave or w.interleave
+    q = ofmt.decode(stored_numpy(case.q[b]), stored_format(case.q))
+    k = ofmt.decode_kv(stored_numpy(case.k[b]), stored_format(case.k[b]), case.k_scale)
+    if case.v is None:
+        v = k[:, :, :w.head_dim_v]
+    else:
+        v = ofmt.decode_kv(stored_numpy(case.v[b]), stored_format(case.v[b]), case.v_scale)
+    full = oatt.decode_attention(q, k, v, w.softmax_scale, case.sink)
+    parts = None
+    if with_partials:
+        own = olay.owners(int(case.seq_lens[b]), w.block_size, D, I)
+        parts = oatt.rank_partials(q, k, v, w.softmax_scale, own, D)
+    return full, parts
+
+
+def check_rows(got, ref, tol, what, out_bf16=False):
+    """Element-wise max-abs and per-row relative bounds for [H, Dv] outputs."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    max_abs = tol["max_abs"]
+    assert err.max() <= max_abs, f"{what}: max-abs {err.max():.3e} > {max_abs}"
+    rel_tol = tol["row_rel"] + (OUT_BF16_EXTRA if out_bf16 else 0.0)
+    row_ref = np.maximum(np.abs(ref).max(axis=-1), 1e-3)
+    rel = err.max(axis=-1) / row_ref
+    assert rel.max() <= rel_tol, f"{what}: row-relative {rel.max():.3e} > {rel_tol}"
+
+
+def check_lse(got, ref, tol, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    inf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf_ref), f"{what}: -inf pattern differs"
+    d = np.abs(got[~inf_ref] - ref[~inf_ref])
+    if d.size:
+        assert d.max() <= tol["lse"], f"{what}: LSE err {d.max():.3e} > {tol['lse']}"
+
+
+def check_against_oracle(inputs, result, requests=None, check_parts=True, rank_begin=0):
+    case, w = inputs.case, inputs.w
+    po, pl, o, lse = [t.float().cpu().numpy() for t in result]
+    tol = TOL[w.kv_format]
+    R = po.shape[0]
+    for b in (range(case.batch) if requests is None else requests):
+        (fo, fl), parts = oracle_request(case, b, inputs.D, inputs.I, with_partials=check_parts)
+        if R == inputs.D:
+            check_rows(o[b], fo, tol, f"merged O b={b}", out_bf16=(w.out_format == "bf16"))
+            check_lse(lse[b], fl, tol, f"merged LSE b={b}")
+        if check_parts:
+            ro, rl = parts
+            for r in range(R):
+                check_rows(po[r, b], ro[rank_begin + r], tol, f"partial O r={rank_begin + r} b={b}")
+                check_lse(pl[r, b], rl[rank_begin + r], tol, f"partial LSE r={rank_begin + r} b={b}")

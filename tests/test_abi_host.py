@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any launch
+(so these calls never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sequence_sharded_paged_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcp.h")
+
+INV, UNS, WS = native.DCP_ERR_INVALID_ARG, native.DCP_ERR_UNSUPPORTED, native.DCP_ERR_WORKSPACE
+NULL = None
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(native.LIB_PATH):
+        pytest.skip("libdcp.so not built")
+    return native.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared()
+    assert declared, "no declarations found"
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in dcp.h but not exported"
+    assert set(declared) == set(native.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert native.dcp_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert native.status_string(st) not in ("", "unknown status")
+    assert native.status_string(-99) == "unknown status"
+
+
+def _fake(n=16):
+    # host buffers: validation rejects the call before any pointer is read
+    return ctypes.c_void_p(ctypes.addressof((ctypes.c_char * n)()))
+
+
+def test_local_seq_lens_validation(L):
+    p = _fake()
+    assert L.dcp_local_seq_lens(p, 4, 4, 2, 3, p, NULL) == INV      # block_size % interleave
+    assert L.dcp_local_seq_lens(p, 4, 4, 0, 1, p, NULL) == INV      # dcp_size
+    assert L.dcp_local_seq_lens(p, 4, 4, 2, 0, p, NULL) == INV      # interleave
+    assert L.dcp_local_seq_lens(p, -1, 4, 2, 1, p, NULL) == INV     # num_reqs
+    assert L.dcp_local_seq_lens(NULL, 4, 4, 2, 1, p, NULL) == INV   # null
+    assert L.dcp_local_seq_lens(NULL, 0, 4, 2, 1, NULL, NULL) == 0  # empty: nothing launched
+
+
+def test_slot_mapping_validation(L):
+    p = _fake()
+    f = L.dcp_slot_mapping
+    assert f(p, p, 8, p, 2, 4, 4, 16, 4, 3, p, NULL) == INV         # 16 % 3
+    assert f(p, p, 8, p, 2, 2, 4, 16, 4, 1, p, NULL) == INV         # stride < max_vblocks
+    assert f(p, p, -1, p, 2, 4, 4, 16, 4, 1, p, NULL) == INV        # negative tokens
+    assert f(NULL, p, 8, p, 2, 4, 4, 16, 4, 1, p, NULL) == INV      # null positions
+    assert f(p, p, 8, NULL, 2, 4, 4, 16, 4, 1, p, NULL) == INV      # null table
+    assert f(p, p, 0, p, 2, 4, 4, 16, 4, 1, p, NULL) == 0           # empty
+
+
+def _kv(**kw):
+    d = native.KvCache()
+    d.dtype, d.num_blocks, d.block_size, d.num_kv_heads = native.DCP_BF16, 8, 16, 2
+    d.head_dim_k, d.head_dim_v = 128, 128
+    d.k = 4096
+    d.v = 8192
+    for i, s in enumerate((8 * 2 * 16 * 128, 2 * 16 * 128, 16 * 128, 128, 1)):
+        d.k_stride[i] = s
+    for i, s in enumerate((8 * 2 * 16 * 128, 2 * 16 * 128, 16 * 128, 1, 16)):
+        d.v_stride[i] = s
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _ws(L, kv, batch=4, hq=8, qd=native.DCP_BF16, rc=2, algo=0):
+    st = ctypes.c_int(123)
+    n = L.dcp_partial_decode_attn_workspace_size(batch, hq, qd, ctypes.byref(kv), rc, algo, ctypes.byref(st))
+    return st.value, n
+
+
+def test_workspace_size_is_host_only(L):
+    st, n = _ws(L, _kv())
+    assert st == 0 and n > 0                      # MFMA path needs a plan + partials
+    st, n = _ws(L, _kv(), algo=native.DCP_ALGO_GENERIC)
+    assert st == 0 and n == 0
+    st, n = _ws(L, _kv(), hq=7)
+    assert st == INV and n == 0                   # Hq % Hkv
+    st, _ = _ws(L, _kv(dtype=native.DCP_FP8_E4M3))
+    assert st == INV                              # fp8 without scales
+    st, _ = _ws(L, _kv(dtype=7))
+    assert st == UNS
+    st, _ = _ws(L, _kv(v=None, head_dim_v=256))
+    assert st == INV                              # aliased V longer than K
+    st, _ = _ws(L, _kv(head_dim_k=2048))
+    assert st == UNS
+    st, _ = _ws(L, _kv(), algo=9)
+    assert st == INV
+    st, _ = _ws(L, _kv(head_dim_k=64, head_dim_v=64), algo=native.DCP_ALGO_FAST)
+    assert st == UNS                              # no MFMA kernel for d=64
+
+
+def test_partial_attn_validation(L):
+    p = _fake(64)
+    kv = _kv()
+    f = L.dcp_partial_decode_attn
+
+    def call(batch=4, hq=8, bt_stride=4, max_vb=4, dcp=4, rb=0, rc=2, scale=0.1, ws=p, ws_bytes=1 << 40,
+             q=p, out=p):
+        return f(q, native.DCP_BF16, batch, hq, ctypes.byref(kv), p, bt_stride, max_vb, p, dcp, rb, rc,
+                 ctypes.c_float(scale), 0, out, p, ws, ctypes.c_size_t(ws_bytes), NULL)
+
+    assert call(rb=3, rc=2) == INV                 # rank range past dcp_size
+    assert call(rb=-1) == INV
+    assert call(rc=0) == INV
+    assert call(bt_stride=2) == INV
+    assert call(scale=float("inf")) == INV
+    assert call(q=NULL) == INV
+    assert call(out=NULL) == INV
+    assert call(ws_bytes=16) == WS                 # workspace too small
+    assert call(batch=0) == 0                      # empty batch: nothing launched
+
+
+def test_merge_validation(L):
+    p = _fake()
+    f = L.dcp_lse_merge
+    assert f(p, p, 0, 2, 4, 8, NULL, 0, p, p, NULL) == INV      # no parts
+    assert f(p, p, 65, 2, 4, 8, NULL, 0, p, p, NULL) == INV     # too many parts
+    assert f(p, p, 2, 2, 0, 8, NULL, 0, p, p, NULL) == INV      # heads
+    assert f(p, p, 2, 2, 4, 8, NULL, 2, p, p, NULL) == UNS      # fp8 output
+    assert f(NULL, p, 2, 2, 4, 8, NULL, 0, p, p, NULL) == INV
+    assert f(NULL, NULL, 2, 0, 4, 8, NULL, 0, NULL, NULL, NULL) == 0

@@ -1,0 +1,202 @@
+"""GPU parity: every HIP kernel against the CPU oracle, through the C ABI.
+
+Integer work (local lengths, slot mapping) must be bit-exact; attention must
+meet the tolerances in harness.TOL on both the per-rank partials and the
+merged result. Pools are pre-filled with NaN bit patterns so that any read of
+a slot the layout did not fill poisons the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sequence_sharded_paged_amd as dcp
+from oracle import attention as oatt
+from oracle import formats as ofmt
+from oracle import layout as olay
+from workloads import get_workload, make_case
+from tests.harness import DeviceInputs, check_against_oracle, check_lse, check_rows, TOL
+
+pytestmark = pytest.mark.gpu
+
+GEN, FAST = dcp.DCP_ALGO_GENERIC, dcp.DCP_ALGO_FAST
+
+
+# ---------------------------------------------------------------------------
+# slot mapping and local lengths (bit-exact)
+# ---------------------------------------------------------------------------
+LAYOUTS = [(bs, D, I) for bs in (1, 2, 16, 64) for D in (1, 2, 3, 4, 8) for I in (1, 2, 16, 64) if bs % I == 0]
+
+
+@pytest.mark.parametrize("bs,D,I", LAYOUTS)
+def test_local_seq_lens_bitexact(device, bs, D, I):
+    rng = np.random.default_rng(bs * 1000 + D * 10 + I)
+    lens = np.concatenate([[0, 1, 2, bs * D - 1, bs * D, bs * D + 1, 1 << 20, (1 << 20) + 37],
+                           rng.integers(0, 300000, size=40)]).astype(np.int32)
+    got = dcp.dcp_local_seq_lens(torch.from_numpy(lens).to(device), bs, D, I).cpu().numpy()
+    ref = olay.local_seq_lens(lens, bs, D, I)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("bs,D,I", LAYOUTS)
+def test_slot_mapping_bitexact(device, bs, D, I):
+    rng = np.random.default_rng(bs * 7 + D * 3 + I)
+    span = bs * D
+    lens = [1, span - 1, 3 * span + 5, 600]
+    nvb = [(L + span - 1) // span for L in lens]
+    width = max(nvb) + 2
+    table = np.full((len(lens), width), -1, dtype=np.int32)
+    perm = rng.permutation(sum(nvb) + 5).astype(np.int32)
+    pos = 0
+    for b, n in enumerate(nvb):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    table[3, 1] = -1                                           # a hole: unallocated block
+    positions = np.concatenate([np.arange(L) for L in lens] + [[-1, -5, width * span, width * span + 3, 7, 0]])
+    reqs = np.concatenate([np.full(L, b) for b, L in enumerate(lens)] + [[0, 1, 2, 3, 9, -1]])
+    got = dcp.dcp_slot_mapping(torch.from_numpy(positions.astype(np.int64)).to(device),
+                               torch.from_numpy(reqs.astype(np.int32)).to(device),
+                               torch.from_numpy(table).to(device), bs, D, I).cpu().numpy()
+    ref = olay.slot_mapping(positions, reqs, table, bs, D, I)
+    assert np.array_equal(got, ref)
+
+
+def test_slot_mapping_max_vblocks_bound(device):
+    table = np.arange(12, dtype=np.int32).reshape(2, 6)
+    positions = np.arange(0, 96, 5, dtype=np.int64)
+    reqs = np.zeros_like(positions, dtype=np.int32)
+    got = dcp.dcp_slot_mapping(torch.from_numpy(positions).to(device), torch.from_numpy(reqs).to(device),
+                               torch.from_numpy(table).to(device), 4, 2, 2, max_vblocks=3).cpu().numpy()
+    ref = olay.slot_mapping(positions, reqs, table, 4, 2, 2, max_vblocks=3)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# LSE merge
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R,with_sink,out", [(1, False, torch.float32), (2, True, torch.float32),
+                                              (8, True, torch.bfloat16), (8, False, torch.bfloat16),
+                                              (5, True, torch.float32), (64, False, torch.float32)])
+def test_lse_merge(device, R, with_sink, out):
+    rng = np.random.default_rng(R * 10 + with_sink)
+    B, H, Dv = 3, 16, 72
+    po = rng.standard_normal((R, B, H, Dv)).astype(np.float32)
+    pl = (rng.standard_normal((R, B, H)) * 4).astype(np.float32)
+    pl[rng.random((R, B, H)) < 0.3] = -np.inf                 # empty shards
+    pl[:, 0, 0] = -np.inf                                      # an all-empty head
+    po[np.isneginf(pl)] = 0.0
+    sink = (rng.standard_normal(H) + 1).astype(np.float32) if with_sink else None
+    o, lse = dcp.dcp_lse_merge(torch.from_numpy(po).to(device), torch.from_numpy(pl).to(device),
+                               sink=None if sink is None else torch.from_numpy(sink).to(device), out_dtype=out)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        ro, rl = oatt.lse_merge(po[:, b], pl[:, b], sink)
+        tol = dict(max_abs=1e-5 if out == torch.float32 else 2e-2, row_rel=1e-5, lse=1e-5)
+        check_rows(o[b], ro, tol, f"merge b={b}", out_bf16=(out == torch.bfloat16))
+        check_lse(lse[b], rl, tol, f"merge lse b={b}")
+
+
+# ---------------------------------------------------------------------------
+# partial attention + merge, reduced sizes with the workloads' geometry
+# ---------------------------------------------------------------------------
+SMALL = {
+    "gqa_fp32_tiny": [None],
+    "gqa_bf16_32k": [[1, 15, 16, 17, 31, 32, 33, 100, 257, 1000, 4099, 0]],
+    "gqa_fp8_binned": [[1, 63, 64, 65, 511, 512, 513, 3000, 0, 10000, 129, 2]],
+    "mla_bf16_bimodal": [[1, 63, 64, 65, 700, 0, 2000]],
+    "mla_bf16_longtail_sink": [[1, 5, 37, 600, 1500]],
+}
+
+
+def _algos(name):
+    return [GEN, FAST] if name in ("gqa_bf16_32k", "gqa_fp8_binned") else [GEN]
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_attention_small(device, name):
+    w = get_workload(name)
+    for lens in SMALL[name]:
+        case = make_case(w, device=device, seq_lens=lens)
+        inp = DeviceInputs(case, device)
+        for algo in _algos(name):
+            res = inp.run(algo=algo)
+            check_against_oracle(inp, res)
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_longtail_sink"])
+def test_rank_subsets(device, name):
+    """One GPU computing only its own rank(s), as a per-GPU deployment would."""
+    w = get_workload(name)
+    case = make_case(w, device=device, seq_lens=[70, 1, 300, 2000, 0])
+    inp = DeviceInputs(case, device)
+    for algo in _algos(name):
+        for rb, rc in [(0, 1), (1, 2), (inp.D - 1, 1)]:
+            res = inp.run(algo=algo, rank_begin=rb, rank_count=rc)
+            check_against_oracle(inp, res, rank_begin=rb)
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned"])
+def test_invariance_over_dcp_and_interleave(device, name):
+    """The merged result does not depend on dcp_size or the interleave size."""
+    w = get_workload(name)
+    case = make_case(w, device=device, seq_lens=[777, 64, 5000, 1])
+    outs = []
+    bs = w.block_size
+    for D, I in [(1, 1), (2, 1), (3, bs), (4, bs // 2), (8, bs), (8, 1)]:
+        inp = DeviceInputs(case, device, dcp_size=D, interleave=I)
+        res = inp.run(algo=FAST)
+        check_against_oracle(inp, res, check_parts=False)
+        outs.append(res[2].float().cpu().numpy())
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 2e-2
+
+
+def test_all_empty_batch(device):
+    w = get_workload("gqa_fp8_binned")
+    case = make_case(w, device=device, seq_lens=[0, 0, 0])
+    inp = DeviceInputs(case, device)
+    for algo in (GEN, FAST):
+        po, pl, o, lse = inp.run(algo=algo)
+        assert torch.all(po == 0) and torch.all(torch.isneginf(pl))
+        assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_token_major_v_layout_uses_generic(device):
+    w = get_workload("gqa_bf16_32k")
+    case = make_case(w, device=device, seq_lens=[100, 33])
+    inp = DeviceInputs(case, device, v_layout="token_major")
+    check_against_oracle(inp, inp.run(algo=dcp.DCP_ALGO_AUTO))
+    with pytest.raises(dcp.DcpError):
+        inp.run(algo=FAST)
+
+
+def test_fp8_codes_exhaustive(device):
+    """Every finite e4m3 code, through the value path with one token per
+    request (weight exactly 1): the partial output is code * v_scale exactly."""
+    w = get_workload("gqa_fp8_binned")
+    case = make_case(w, device=device, seq_lens=[1, 1])
+    codes = np.arange(256, dtype=np.uint8)
+    codes[codes == 0x7F] = 0
+    codes[codes == 0xFF] = 0
+    for b in range(2):
+        v = np.tile(codes[128 * b:128 * (b + 1)], (1, w.num_kv_heads, 1))
+        case.v[b] = torch.from_numpy(v).to(device).view(torch.float8_e4m3fn)
+    inp = DeviceInputs(case, device)
+    tab = ofmt.e4m3fn_table()
+    for algo in (GEN, FAST):
+        po = inp.run(algo=algo)[0].cpu().numpy()           # [R, B, Hq, Dv]
+        for b in range(2):
+            owner = 0                                        # token 0 lives on rank 0
+            for h in range(w.num_q_heads):
+                ref = tab[codes[128 * b:128 * (b + 1)]] * np.float64(case.v_scale[h // w.group])
+                np.testing.assert_allclose(po[owner, b, h], ref, rtol=2e-7, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+def test_full_gqa_bf16_32k_all_requests(device):
+    w = get_workload("gqa_bf16_32k")
+    case = make_case(w, device=device)
+    inp = DeviceInputs(case, device)
+    check_against_oracle(inp, inp.run(algo=FAST))
