@@ -7,14 +7,8 @@
 // for Long Context Workloads", section 5.4 (the query heads of a group share
 // one KV head).
 //
-// Work split ("stream-K"): a unit is (rank, request, KV head); its local
-// tokens are cut into tiles of TOK tokens; the tiles of all units, in unit
-// order, are dealt out in equal contiguous ranges to persistent wavefronts.
-// A wavefront that covers a whole unit writes the unit's final (O, LSE); a
-// unit cut between wavefronts leaves up to one unnormalised partial per side
-// in the workspace and a combine kernel merges them by log-sum-exp. A planner
-// kernel builds the tile prefix over units on the device, so the grid depends
-// only on the device, never on the lengths (graph-safe).
+// Work split: stream-K over (rank, request, KV head) units (splitkv.h) with
+// one persistent wavefront per worker and tiles of TOK tokens.
 //
 // Per wavefront and tile, with lane l = 16*qd + n (n = l % 16, qd = l / 16):
 //   scores  S^T[token, head] = K[token, :] . Q[head, :]   (MFMA 16x16x32 bf16,
@@ -32,21 +26,13 @@
 // product: no LDS, no shuffles besides the max/sum reductions. fp8 codes are
 // widened to bf16 in registers (exact) and the per-head scales are applied to
 // the scores and to the output, outside the dot products.
-#include "common.h"
+#include "splitkv.h"
 
 namespace dcp {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGqaDim = 128;
 constexpr int kGqaMaxWorkers = 8192;
 constexpr int kGqaWavesPerBlock = 4;
-constexpr int kPlanThreads = 1024;
-constexpr int kPartExtra = 3;  // per partial head row: O[128], m (log2 units), rounded sum, fp32 sum
 
 template <bool kFp8>
 struct GqaTile {
@@ -78,74 +64,6 @@ __device__ __forceinline__ u32x4_t keep_bytes(u32x4_t v, int keep) {
   return v;
 }
 
-struct GqaWs {
-  int64_t* prefix;     // [U + 1] tile prefix over units
-  int32_t* wunit;      // [kGqaMaxWorkers] unit holding each worker's first tile
-  float* part;         // [kGqaMaxWorkers][2][group][Dv + kPartExtra]
-};
-
-__host__ __device__ inline GqaWs gqa_ws(void* base, int64_t units) {
-  GqaWs w;
-  char* p = static_cast<char*>(base);
-  w.prefix = reinterpret_cast<int64_t*>(p);
-  p += align_up(static_cast<size_t>(units + 1) * sizeof(int64_t), 256);
-  w.wunit = reinterpret_cast<int32_t*>(p);
-  p += align_up(static_cast<size_t>(kGqaMaxWorkers) * sizeof(int32_t), 256);
-  w.part = reinterpret_cast<float*>(p);
-  return w;
-}
-
-// ---------------------------------------------------------------------------
-// Planner: tile prefix over units and each worker's first unit (one block).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kPlanThreads) gqa_plan_kernel(AttnParams p, int tok, int workers) {
-  __shared__ int64_t scan[kPlanThreads];
-  __shared__ int64_t total_s;
-  const int Hkv = p.kv.num_kv_heads;
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
-  GqaWs ws = gqa_ws(p.workspace, U);
-  const int tid = threadIdx.x;
-  const int64_t chunk = (U + kPlanThreads - 1) / kPlanThreads;
-  const int64_t u0 = min(U, tid * chunk), u1 = min(U, u0 + chunk);
-  auto tiles = [&](int64_t u) -> int64_t {
-    const int64_t rb = u / Hkv;  // r * batch + b
-    const int b = static_cast<int>(rb % p.batch), r = static_cast<int>(rb / p.batch);
-    const int64_t n = max(p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r], 0);
-    return (n + tok - 1) / tok;
-  };
-  int64_t s = 0;
-  for (int64_t u = u0; u < u1; ++u) s += tiles(u);
-  scan[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {  // Hillis-Steele inclusive scan
-    const int64_t v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int64_t run = scan[tid] - s;  // exclusive prefix
-  for (int64_t u = u0; u < u1; ++u) {
-    ws.prefix[u] = run;
-    run += tiles(u);
-  }
-  if (tid == kPlanThreads - 1) {
-    ws.prefix[U] = scan[tid];
-    total_s = scan[tid];
-  }
-  __syncthreads();
-  const int64_t T = total_s;
-  if (T == 0) return;
-  const int64_t tpw = (T + workers - 1) / workers;
-  run = scan[tid] - s;
-  for (int64_t u = u0; u < u1; ++u) {
-    const int64_t nxt = run + tiles(u);
-    // workers whose first tile lies in [run, nxt)
-    for (int64_t w = (run + tpw - 1) / tpw; w < (nxt + tpw - 1) / tpw && w < workers; ++w)
-      ws.wunit[w] = static_cast<int32_t>(u);
-    run = nxt;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Main kernel: one persistent wavefront per worker.
 // ---------------------------------------------------------------------------
@@ -158,7 +76,7 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnPa
   const int n = lane & 15, qd = lane >> 4;
   const int Hkv = p.kv.num_kv_heads, G = p.group;
   const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
-  GqaWs ws = gqa_ws(p.workspace, U);
+  SplitWs ws = split_ws(p.workspace, U, kGqaMaxWorkers);
   const int64_t T = ws.prefix[U];
   if (worker >= workers || T == 0) return;
   const int64_t tpw = (T + workers - 1) / workers;
@@ -356,50 +274,6 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnPa
 }
 
 // ---------------------------------------------------------------------------
-// Combine: merge the pieces of units cut between workers; zero empty units.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(128) gqa_combine_kernel(AttnParams p, int workers) {
-  const int Hkv = p.kv.num_kv_heads, G = p.group;
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
-  const int64_t u = blockIdx.x;
-  GqaWs ws = gqa_ws(p.workspace, U);
-  const int64_t T = ws.prefix[U];
-  const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
-  const int h = static_cast<int>(u % Hkv);
-  const int64_t rb = u / Hkv;
-  const int d = threadIdx.x;
-  if (ubeg == uend) {  // empty shard: O = 0, LSE = -inf
-    for (int g = 0; g < G; ++g) {
-      const int64_t row = rb * p.num_q_heads + static_cast<int64_t>(h) * G + g;
-      p.out_o[row * kGqaDim + d] = 0.f;
-      if (d == 0) p.out_lse[row] = -INFINITY;
-    }
-    return;
-  }
-  const int64_t tpw = (T + workers - 1) / workers;
-  const int64_t wa = ubeg / tpw, wb = (uend - 1) / tpw;
-  if (wa == wb) return;  // written whole by one worker
-  for (int g = 0; g < G; ++g) {
-    float mx = -INFINITY;
-    for (int64_t w = wa; w <= wb; ++w) {
-      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * G + g) * (kGqaDim + kPartExtra);
-      mx = fmaxf(mx, hrow[kGqaDim]);
-    }
-    float acc = 0.f, lsum = 0.f, esum = 0.f;
-    for (int64_t w = wa; w <= wb; ++w) {
-      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * G + g) * (kGqaDim + kPartExtra);
-      const float sc = exp2f(hrow[kGqaDim] - mx);
-      acc += sc * hrow[d];
-      lsum += sc * hrow[kGqaDim + 1];
-      esum += sc * hrow[kGqaDim + 2];
-    }
-    const int64_t row = rb * p.num_q_heads + static_cast<int64_t>(h) * G + g;
-    p.out_o[row * kGqaDim + d] = acc / lsum;
-    if (d == 0) p.out_lse[row] = (mx + __log2f(esum)) * DCP_LN2;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 bool gqa_supported(const AttnParams& p) {
@@ -422,10 +296,7 @@ bool gqa_supported(const AttnParams& p) {
 
 size_t gqa_workspace_bytes(const AttnParams& p) {
   const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
-  size_t b = align_up(static_cast<size_t>(U + 1) * sizeof(int64_t), 256);
-  b += align_up(static_cast<size_t>(kGqaMaxWorkers) * sizeof(int32_t), 256);
-  b += static_cast<size_t>(kGqaMaxWorkers) * 2 * p.group * (kGqaDim + kPartExtra) * sizeof(float);
-  return b;
+  return split_ws_bytes(U, kGqaMaxWorkers, p.group, kGqaDim);
 }
 
 template <bool kFp8>
@@ -447,7 +318,7 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   const int workers = fp8 ? gqa_workers<true>() : gqa_workers<false>();
   const int tok = fp8 ? GqaTile<true>::TOK : GqaTile<false>::TOK;
   const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
-  hipLaunchKernelGGL(gqa_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, tok, workers);
+  hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, tok, workers, kGqaMaxWorkers);
   const dim3 grid((workers + kGqaWavesPerBlock - 1) / kGqaWavesPerBlock);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   if (fp8)
@@ -455,7 +326,8 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   else
     hipLaunchKernelGGL(gqa_attn_kernel<false>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  hipLaunchKernelGGL(gqa_combine_kernel, dim3(static_cast<unsigned>(U)), dim3(kGqaDim), 0, p.stream, p, workers);
+  hipLaunchKernelGGL(split_combine_kernel<kGqaDim>, dim3(static_cast<unsigned>(U)), dim3(256), 0, p.stream, p, workers,
+                     kGqaMaxWorkers);
   return hipGetLastError();
 }
 

@@ -103,13 +103,13 @@ SMALL = {
     "gqa_fp32_tiny": [None],
     "gqa_bf16_32k": [[1, 15, 16, 17, 31, 32, 33, 100, 257, 1000, 4099, 0]],
     "gqa_fp8_binned": [[1, 63, 64, 65, 511, 512, 513, 3000, 0, 10000, 129, 2]],
-    "mla_bf16_bimodal": [[1, 63, 64, 65, 700, 0, 2000]],
-    "mla_bf16_longtail_sink": [[1, 5, 37, 600, 1500]],
+    "mla_bf16_bimodal": [[1, 31, 32, 33, 63, 64, 65, 700, 0, 2000, 4097]],
+    "mla_bf16_longtail_sink": [[1, 5, 37, 600, 1500, 2049]],
 }
 
 
 def _algos(name):
-    return [GEN, FAST] if name in ("gqa_bf16_32k", "gqa_fp8_binned") else [GEN]
+    return [GEN] if name == "gqa_fp32_tiny" else [GEN, FAST]
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
@@ -135,7 +135,7 @@ def test_rank_subsets(device, name):
             check_against_oracle(inp, res, rank_begin=rb)
 
 
-@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned"])
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_bimodal"])
 def test_invariance_over_dcp_and_interleave(device, name):
     """The merged result does not depend on dcp_size or the interleave size."""
     w = get_workload(name)
@@ -200,3 +200,26 @@ def test_full_gqa_bf16_32k_all_requests(device):
     case = make_case(w, device=device)
     inp = DeviceInputs(case, device)
     check_against_oracle(inp, inp.run(algo=FAST))
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_bimodal", "mla_bf16_longtail_sink"])
+def test_large_logit_needles(device, name):
+    """Needle keys scored ~120 above the rest late in the sequence: the MLA
+    kernel's per-piece reference max is outgrown and the piece is replayed;
+    the GQA kernel rescales. The output must follow the needles."""
+    w = get_workload(name)
+    case = make_case(w, device=device, seq_lens=[3000, 129, 5000], needles=2, needle_logit=120.0)
+    inp = DeviceInputs(case, device)
+    for algo in _algos(name):
+        check_against_oracle(inp, inp.run(algo=algo))
+
+
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_bimodal"])
+def test_moderate_needles(device, name):
+    """Needles at logit ~20 on every rank: a misplaced or dropped block shows
+    an error of order one in the needle heads."""
+    w = get_workload(name)
+    case = make_case(w, device=device, seq_lens=[4000, 700, 65, 9000], needles=6, needle_logit=20.0)
+    inp = DeviceInputs(case, device)
+    for algo in _algos(name):
+        check_against_oracle(inp, inp.run(algo=algo))

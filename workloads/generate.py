@@ -154,13 +154,16 @@ def needle_positions(w: Workload, b: int, L: int, count: int) -> np.ndarray:
 def _plant_needles(w, b, L, kb, qb, count, logit, lens):
     """Overwrite a few key rows so one query head of the group scores them at
     about ``logit`` (before the fp8 scale), making the output of that head
-    close to the needle's value row."""
+    close to the needle's value row. For MLA, whose value is the latent part
+    of the key, only the rope part of the key is set, so the value row keeps
+    its N(0, 1) entries."""
     rng = _rng(w.seed, NEEDLES, 100000 + b)
+    lo = w.head_dim_v if w.mla else 0
     for x in needle_positions(w, b, L, count):
         kv = int(rng.integers(0, w.num_kv_heads))
         h = kv * w.group + int(rng.integers(0, w.group))
-        qh = qb[h].float()
-        kb[int(x), kv] = qh * (logit / (w.softmax_scale * float(qh.norm()) ** 2))
+        qh = qb[h, lo:].float()
+        kb[int(x), kv, lo:] = qh * (logit / (w.softmax_scale * float(qh.norm()) ** 2))
 
 
 def stored_numpy(t: torch.Tensor) -> np.ndarray:
