@@ -317,8 +317,7 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   const bool fp8 = p.kv.dtype == DCP_FP8_E4M3;
   const int workers = fp8 ? gqa_workers<true>() : gqa_workers<false>();
   const int tok = fp8 ? GqaTile<true>::TOK : GqaTile<false>::TOK;
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
-  hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, tok, workers, kGqaMaxWorkers);
+  launch_split_plan(p, tok, workers, kGqaMaxWorkers);
   const dim3 grid((workers + kGqaWavesPerBlock - 1) / kGqaWavesPerBlock);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   if (fp8)
@@ -326,8 +325,7 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   else
     hipLaunchKernelGGL(gqa_attn_kernel<false>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  hipLaunchKernelGGL(split_combine_kernel<kGqaDim>, dim3(static_cast<unsigned>(U)), dim3(256), 0, p.stream, p, workers,
-                     kGqaMaxWorkers);
+  launch_split_combine<kGqaDim>(p, workers, kGqaMaxWorkers);
   return hipGetLastError();
 }
 

@@ -377,14 +377,11 @@ size_t mla_workspace_bytes(const AttnParams& p) {
 
 hipError_t launch_mla_attn(const AttnParams& p) {
   const int workers = min(kMlaMaxWorkers, device_cu_count());
-  const int64_t units = static_cast<int64_t>(p.rank_count) * p.batch;
-  hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, kMlaTile, workers,
-                     kMlaMaxWorkers);
+  launch_split_plan(p, kMlaTile, workers, kMlaMaxWorkers);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   hipLaunchKernelGGL(mla_attn_kernel, dim3(workers), dim3(kMlaThreads), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  hipLaunchKernelGGL(split_combine_kernel<kMlaDv>, dim3(static_cast<unsigned>(units)), dim3(256), 0, p.stream, p,
-                     workers, kMlaMaxWorkers);
+  launch_split_combine<kMlaDv>(p, workers, kMlaMaxWorkers);
   return hipGetLastError();
 }
 
