@@ -38,25 +38,45 @@ constexpr int kMlaDk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaHeads = 128;
 constexpr int kMlaTile = 32;                                     // tokens per tile
-constexpr int kMlaStages = 3;                                    // LDS ring depth
+#ifndef DCP_MLA_STAGES
+#define DCP_MLA_STAGES 4
+#endif
+constexpr int kMlaStages = DCP_MLA_STAGES;                       // LDS ring depth (tiles in flight + 1)
 constexpr int kMlaRowBytes = kMlaDk * 2;                         // 1152
-constexpr int kMlaChunks = kMlaRowBytes / 16;                    // 72
 constexpr int kMlaStageBytes = kMlaTile * kMlaRowBytes;          // 36864
 constexpr int kMlaLatBytes = kMlaDv * 2;                         // 1024: latent part of a row (also V)
 constexpr int kMlaRopeOff = kMlaTile * kMlaLatBytes;             // 32768: rope rows follow the latent rows
 constexpr int kMlaRopeBytes = kMlaRowBytes - kMlaLatBytes;       // 128
-constexpr int kMlaThreads = 256;
-constexpr int kMlaDmaRounds = kMlaTile * kMlaChunks / kMlaThreads;  // 9 loads per thread per tile
+#ifndef DCP_MLA_WAVES
+#define DCP_MLA_WAVES 4
+#endif
+constexpr int kMlaWaves = DCP_MLA_WAVES;                         // wavefronts per workgroup (4 or 8)
+constexpr int kMlaThreads = 64 * kMlaWaves;
+constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32 or 16
+constexpr int kMlaHT = kMlaHeadsPerWave / 16;                    // 16-head MFMA tiles per wavefront
+constexpr int kMlaLatRowsPerWave = kMlaTile / kMlaWaves;         // latent rows loaded per wave and tile
 constexpr int kMlaKSteps = kMlaDk / 32;                          // 18
-constexpr int kMlaKStepsReg = kMlaDv / 32;                       // 16 k-steps of Q kept in VGPRs (latent)
-constexpr int kMlaQLdsBytes = kMlaHeads * (kMlaDk - kMlaDv) * 2; // 16 KB: rope part of Q in LDS
+#ifndef DCP_MLA_QREG
+#define DCP_MLA_QREG 16
+#endif
+#ifndef DCP_MLA_KPF
+#define DCP_MLA_KPF 1
+#endif
+#ifndef DCP_MLA_VPF
+#define DCP_MLA_VPF 1
+#endif
+constexpr int kMlaKStepsReg = DCP_MLA_QREG;                      // k-steps of Q kept in VGPRs; the rest in LDS
+constexpr int kMlaKPf = DCP_MLA_KPF;                             // score-operand read distance (k-steps)
+constexpr int kMlaVPf = DCP_MLA_VPF;                             // value-operand read distance (tiles)
+constexpr int kMlaQLdsSteps = kMlaKSteps - kMlaKStepsReg;        // k-steps of Q held in LDS
+constexpr int kMlaQRopeWaveBytes = kMlaHT * kMlaQLdsSteps * 64 * 16;  // per wave
 constexpr int kMlaDvTiles = kMlaDv / 16;                         // 32
 constexpr int kMlaMaxWorkers = 512;
 constexpr float kMlaRefSlack = 64.f;  // log2 units a tile max may exceed the piece's reference
 
-static_assert(kMlaDmaRounds * kMlaThreads == kMlaTile * kMlaChunks, "tile must split evenly");
+static_assert(kMlaWaves == 4 || kMlaWaves == 8, "4 or 8 wavefronts");
+static_assert(kMlaKStepsReg % 4 == 0 && kMlaKStepsReg <= 16, "latent k-steps in registers");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // Uniform read-only load through the constant address space (scalar load).
@@ -99,12 +119,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int lat_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 __device__ __forceinline__ int rope_swz(int row) { return row & 7; }
 
-__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads),
+                               amdgpu_waves_per_eu(kMlaWaves / 4, kMlaWaves / 4)))
 mla_attn_kernel(AttnParams p, int workers) {
   __shared__ __attribute__((aligned(16))) char lds[kMlaStages * kMlaStageBytes];
-  // rope part of Q in operand order: [wave][hh][ks - 16][lane] x 16 bytes
-  __shared__ __attribute__((aligned(16))) char qrope[kMlaQLdsBytes];
-  __shared__ int votes[4];  // per wave: a head's max outgrew the piece's reference
+  // rope part of Q in operand order: [wave][ks - 16][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) char qrope[kMlaWaves * kMlaQRopeWaveBytes];
+  // The replay vote of wave w lives in the first 4 bytes of w's own Q slice:
+  // by the time a wave votes it no longer reads its slice, and the slice is
+  // refilled only after every wave has read the votes.
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int n = lane & 15, g = lane >> 4;
@@ -122,56 +145,78 @@ mla_attn_kernel(AttnParams p, int workers) {
   const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks3 = p.kv.k_stride[3];
   const char* kbase = static_cast<const char*>(p.kv.k);
   const float c2 = p.softmax_scale * DCP_LOG2E;
+  const bool rope_loader = wave < 4;   // waves 0..3 also load the rope rows (8 rows each)
+  (void)rope_loader;
 
   // ---- tile prefetch (uniform control flow) --------------------------------
   int64_t pf_u = ld_uniform(ws.wunit + worker);
   int64_t pf_t = wstart;
   auto issue = [&](int stage) {
     while (ld_uniform(ws.prefix + pf_u + 1) <= pf_t) ++pf_u;
-    const int64_t lt = pf_t - ld_uniform(ws.prefix + pf_u);
-    const int b = static_cast<int>(pf_u % p.batch), r = static_cast<int>(pf_u / p.batch);
+    const int lt = static_cast<int>(pf_t - ld_uniform(ws.prefix + pf_u));
+    const int uu = static_cast<int>(pf_u);
+    const int b = uu % p.batch, r = uu / p.batch;
     const int len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r);
-    const int t0 = static_cast<int>(lt) * kMlaTile;
+    const int t0 = lt * kMlaTile;
     const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-    // tokens t0..t0+15 share one block and so do t0+16..t0+31 (block_size % 16 == 0);
-    // rows past the end re-read the last token (finite data, zero weight)
-    const int64_t blk_a = ld_uniform(bt + t0 / bs);
-    const int64_t blk_b = ld_uniform(bt + min(t0 + 16, len - 1) / bs);
+    // tokens t0..t0+15 share one block and so do t0+16..t0+31 (block_size %
+    // 16 == 0); a row past the end re-reads token t0 (finite data, zero weight)
+    const int vb_a = t0 / bs, off_a = t0 - vb_a * bs;
+    const bool has_b = t0 + 16 < len;
+    const int vb_b = has_b ? (t0 + 16) / bs : vb_a;
+    const int off_b = has_b ? t0 + 16 - vb_b * bs : off_a;
+    const int64_t base_a = ld_uniform(bt + vb_a) * ks1 + static_cast<int64_t>(off_a) * ks3;
+    const int64_t base_b = ld_uniform(bt + vb_b) * ks1 + static_cast<int64_t>(off_b) * ks3;
     const char* rank_k = kbase + r * ks0 * 2;
     char* dst = lds + stage * kMlaStageBytes;
-    // rounds 0..7: latent row 8*wave + k, lane = destination slot (uniform row per instruction)
+    // latent rows: one row per instruction (uniform address), lane = destination slot
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int row = 8 * wave + k;
-      const int tok = min(t0 + row, len - 1);
-      const int64_t blk = row < 16 ? blk_a : blk_b;
-      const char* src = rank_k + (blk * ks1 + static_cast<int64_t>(tok % bs) * ks3) * 2 + 16 * (lane ^ lat_swz(row));
-      dma16(src, lds_addr(dst + row * kMlaLatBytes));
+    for (int k = 0; k < kMlaLatRowsPerWave; ++k) {
+      const int row = kMlaLatRowsPerWave * wave + k;
+      const int64_t el = (t0 + row < len) ? (row < 16 ? base_a : base_b) + (row & 15) * ks3 : base_a;
+      dma16(rank_k + el * 2 + 16 * (lane ^ lat_swz(row)), lds_addr(dst + row * kMlaLatBytes));
     }
-    // round 8: rope rows 8*wave .. 8*wave+7, 8 chunks each
-    {
+    // rope rows 8*wave .. 8*wave+7 (waves 0..3), 8 chunks each
+    if (rope_loader) {
       const int row = 8 * wave + (lane >> 3);
-      const int tok = min(t0 + row, len - 1);
-      const int64_t blk = wave < 2 ? blk_a : blk_b;
-      const char* src = rank_k + (blk * ks1 + static_cast<int64_t>(tok % bs) * ks3) * 2 + kMlaLatBytes +
-                        16 * ((lane & 7) ^ rope_swz(row));
-      dma16(src, lds_addr(dst + kMlaRopeOff + 8 * wave * kMlaRopeBytes));
+      const int64_t el = (t0 + row < len) ? (wave < 2 ? base_a : base_b) + (row & 15) * ks3 : base_a;
+      dma16(rank_k + el * 2 + kMlaLatBytes + 16 * ((lane & 7) ^ rope_swz(row)),
+            lds_addr(dst + kMlaRopeOff + 8 * wave * kMlaRopeBytes));
     }
     ++pf_t;
   };
+  // this thread's DMA count per tile (for the vmcnt waits)
+  // waits until this thread's loads of the current tile have landed; `ahead`
+  // younger tiles (0 .. stages-2) may stay in flight
+  auto wait_tile = [&](int ahead) {
+    constexpr int a = kMlaLatRowsPerWave + 1, b = kMlaLatRowsPerWave;
+    if (ahead <= 0) wait_vmcnt<0>();
+    else if (ahead == 1) { if (rope_loader) wait_vmcnt<a>(); else wait_vmcnt<b>(); }
+    else if (ahead == 2 || kMlaStages < 4) { if (rope_loader) wait_vmcnt<2 * a>(); else wait_vmcnt<2 * b>(); }
+    else { if (rope_loader) wait_vmcnt<3 * a>(); else wait_vmcnt<3 * b>(); }
+  };
 
-  issue(0);
-  if (wstart + 1 < wend) issue(1);
+  for (int j = 0; j < kMlaStages - 1 && wstart + j < wend; ++j) issue(j);
 
   int64_t cur_u = ld_uniform(ws.wunit + worker);  // unit of the tile being computed
   int64_t tile = wstart;
-  float m_hint[2] = {-INFINITY, -INFINITY};  // reference for a replayed piece
   int stage = 0;
-  const int sw_k = lat_swz(n);                     // swizzle of this lane's score-operand rows (16u + n)
-  const int sw_rope = rope_swz(n);
+  float m_hint[kMlaHT];  // reference for a replayed piece
+#pragma unroll
+  for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = -INFINITY;
+  // per-lane LDS byte offsets (the swizzles only touch the low 4 bits of a
+  // chunk index, so the rest of each address is an immediate)
+  // score operand, k-step ks: row n, chunk (4ks + g) ^ lat_swz(n) =
+  //   koff(ks & 3) + 256 * (ks >> 2) bytes; value operand, tile nt: row tr_row,
+  //   chunk (2nt + tr_j / 2) ^ lat_swz(tr_row) = troff(nt & 7) + 256 * (nt >> 3)
+  const int kroff = kMlaRopeOff + n * kMlaRopeBytes;
   const int tr_row = 4 * g + (n >> 2);             // LDS row (u = 0) of this lane's transpose read
-  const int sw_tr = lat_swz(tr_row);
   const int tr_j = n & 3;
+  auto koff = [&](int j) { return n * kMlaLatBytes + 16 * ((4 * j + g) ^ lat_swz(n)); };
+  auto troff = [&](int j) {
+    return tr_row * kMlaLatBytes + 8 * (tr_j & 1) + 16 * ((2 * j + (tr_j >> 1)) ^ lat_swz(tr_row));
+  };
+  char* qr = qrope + wave * kMlaQRopeWaveBytes + lane * 16;
 
   while (tile < wend) {
     while (ld_uniform(ws.prefix + cur_u + 1) <= tile) ++cur_u;
@@ -181,21 +226,20 @@ mla_attn_kernel(AttnParams p, int workers) {
     const int len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin +
                                static_cast<int>(cur_u / p.batch));
 
-    // Q operand (B of the score MFMA): head 32*wave + 16*hh + n, dims 32*ks + 8*g .. +8
-    // (latent k-steps in VGPRs, rope k-steps in this wave's slice of LDS)
-    bf16x8_t qop[2][kMlaKStepsReg];
-    char* qr = qrope + wave * 4096 + lane * 16;
+    // Q operand (B of the score MFMA): head 16*wave + n, dims 32*ks + 8*g .. +8;
+    // latent k-steps in VGPRs, rope k-steps in this wave's slice of LDS
+    bf16x8_t qop[kMlaHT][kMlaKStepsReg];
     {
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) +
-                           (static_cast<int64_t>(b) * kMlaHeads + 32 * wave + n) * kMlaDk + 8 * g;
+                           (static_cast<int64_t>(b) * kMlaHeads + kMlaHeadsPerWave * wave + n) * kMlaDk + 8 * g;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int hh = 0; hh < kMlaHT; ++hh) {
 #pragma unroll
         for (int ks = 0; ks < kMlaKStepsReg; ++ks)
           qop[hh][ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
 #pragma unroll
         for (int ks = kMlaKStepsReg; ks < kMlaKSteps; ++ks)
-          *reinterpret_cast<bf16x8_t*>(qr + (hh * 2 + ks - kMlaKStepsReg) * 1024) =
+          *reinterpret_cast<bf16x8_t*>(qr + (hh * (kMlaKSteps - kMlaKStepsReg) + ks - kMlaKStepsReg) * 1024) =
               *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
       }
     }
@@ -210,63 +254,83 @@ mla_attn_kernel(AttnParams p, int workers) {
     // reference by more than that, the workgroup replays the piece with the
     // largest max seen as the reference (m_hint).
     const int64_t piece_tile0 = tile, piece_u0 = cur_u;
-    float m_ref[2] = {m_hint[0], m_hint[1]}, m_seen[2] = {m_hint[0], m_hint[1]};
-    float l[2] = {0.f, 0.f}, e[2] = {0.f, 0.f};
-    f32x4_t o[2][kMlaDvTiles];
+    float m_ref[kMlaHT], m_seen[kMlaHT], l[kMlaHT], e[kMlaHT];
+    f32x4_t o[kMlaHT][kMlaDvTiles];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < kMlaHT; ++hh) {
+      m_ref[hh] = m_hint[hh];
+      m_seen[hh] = m_hint[hh];
+      l[hh] = 0.f;
+      e[hh] = 0.f;
 #pragma unroll
       for (int nt = 0; nt < kMlaDvTiles; ++nt) o[hh][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     bool bad = false;
     for (int64_t lt = lt_lo; lt < lt_hi; ++lt, ++tile) {
-      if (tile + 1 < wend) wait_vmcnt<kMlaDmaRounds>();
-      else wait_vmcnt<0>();
+      wait_tile(static_cast<int>(min<int64_t>(wend - 1 - tile, kMlaStages - 2)));
       block_sync();
-      if (tile + 2 < wend) issue(stage == 0 ? 2 : stage - 1);
+      if (tile + kMlaStages - 1 < wend) issue(stage == 0 ? kMlaStages - 1 : stage - 1);
       const char* st = lds + stage * kMlaStageBytes;
 
-      // ---- scores -----------------------------------------------------------
-      f32x4_t s[2][2];
+      // ---- scores S^T[token 16u + 4g + i][head n] ----------------------------
+      // The K operand of k-step ks+1 is read before the MFMAs of step ks.
+      // per-tile operand bases; everything else of an address is an immediate
+      const char* kb[4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int j = 0; j < 4; ++j) kb[j] = st + koff(j);
+      const char* krb[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) s[hh][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) krb[j] = st + kroff + 16 * ((4 * j + g) ^ rope_swz(n));
+      auto kaddr = [&](int ks, int u) -> const char* {
+        return ks < kMlaDv / 32 ? kb[ks & 3] + 256 * (ks >> 2) + u * 16 * kMlaLatBytes
+                                : krb[ks - kMlaDv / 32] + u * 16 * kMlaRopeBytes;
+      };
+      f32x4_t s[kMlaHT][2];
+#pragma unroll
+      for (int hh = 0; hh < kMlaHT; ++hh) s[hh][0] = s[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      bf16x8_t ka[kMlaKPf + 1][2];
+#pragma unroll
+      for (int j = 0; j < kMlaKPf; ++j) {
+        ka[j][0] = *reinterpret_cast<const bf16x8_t*>(kaddr(j, 0));
+        ka[j][1] = *reinterpret_cast<const bf16x8_t*>(kaddr(j, 1));
+      }
 #pragma unroll
       for (int ks = 0; ks < kMlaKSteps; ++ks) {
-        bf16x8_t b0, b1;
-        const char* arow;
-        if (ks < kMlaKStepsReg) {
-          b0 = qop[0][ks];
-          b1 = qop[1][ks];
-          arow = st + n * kMlaLatBytes + 16 * ((4 * ks + g) ^ sw_k);
-        } else {
-          b0 = *reinterpret_cast<const bf16x8_t*>(qr + (ks - kMlaKStepsReg) * 1024);
-          b1 = *reinterpret_cast<const bf16x8_t*>(qr + (2 + ks - kMlaKStepsReg) * 1024);
-          arow = st + kMlaRopeOff + n * kMlaRopeBytes + 16 * ((4 * (ks - kMlaKStepsReg) + g) ^ sw_rope);
+        if (ks + kMlaKPf < kMlaKSteps) {
+          ka[(ks + kMlaKPf) % (kMlaKPf + 1)][0] = *reinterpret_cast<const bf16x8_t*>(kaddr(ks + kMlaKPf, 0));
+          ka[(ks + kMlaKPf) % (kMlaKPf + 1)][1] = *reinterpret_cast<const bf16x8_t*>(kaddr(ks + kMlaKPf, 1));
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              arow + u * 16 * (ks < kMlaKStepsReg ? kMlaLatBytes : kMlaRopeBytes));
-          s[0][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, s[0][u], 0, 0, 0);
-          s[1][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, s[1][u], 0, 0, 0);
+        for (int hh = 0; hh < kMlaHT; ++hh) {
+          const bf16x8_t bq = ks < kMlaKStepsReg
+                                  ? qop[hh][ks < kMlaKStepsReg ? ks : 0]
+                                  : *reinterpret_cast<const bf16x8_t*>(
+                                        qr + (hh * (kMlaKSteps - kMlaKStepsReg) + ks - kMlaKStepsReg) * 1024);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            s[hh][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % (kMlaKPf + 1)][u], bq, s[hh][u], 0, 0, 0);
         }
       }
 
-      // ---- softmax weights (log2 units, fixed reference) --------------------
+      // ---- softmax weights (log2 units, fixed reference) ----------------------
       const int tok0 = static_cast<int>(lt) * kMlaTile + 4 * g;   // + 16u + i
-      bf16x8_t pop[2];
+      const bool partial = static_cast<int>(lt) * kMlaTile + kMlaTile > len;   // uniform
+      bf16x8_t pop[kMlaHT];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float mt = -INFINITY;
+      for (int hh = 0; hh < kMlaHT; ++hh) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = (tok0 + 16 * u + i < len) ? s[hh][u][i] * c2 : -INFINITY;
-            s[hh][u][i] = x;
-            mt = fmaxf(mt, x);
-          }
+          for (int i = 0; i < 4; ++i) s[hh][u][i] *= c2;
+        if (partial) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tok0 + 16 * u + i >= len) s[hh][u][i] = -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s[hh][0][0], s[hh][0][1]), fmaxf(s[hh][0][2], s[hh][0][3])),
+                         fmaxf(fmaxf(s[hh][1][0], s[hh][1][1]), fmaxf(s[hh][1][2], s[hh][1][3])));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         m_seen[hh] = fmaxf(m_seen[hh], mt);
@@ -276,7 +340,8 @@ mla_attn_kernel(AttnParams p, int workers) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float pe = exp2f(s[hh][u][i] - m_ref[hh]);
+            // v_exp_f32: exact enough for weights, flushes results below 2^-126 to 0
+            const float pe = __builtin_amdgcn_exp2f(s[hh][u][i] - m_ref[hh]);
             const __bf16 pb = static_cast<__bf16>(pe);
             pop[hh][4 * u + i] = pb;
             l[hh] += static_cast<float>(pb);
@@ -284,29 +349,43 @@ mla_attn_kernel(AttnParams p, int workers) {
           }
       }
 
-      // ---- values -------------------------------------------------------------
-      const char* tr0 = st + tr_row * kMlaLatBytes + 8 * (tr_j & 1);
-      const char* tr1 = tr0 + 16 * kMlaLatBytes;
+      // ---- values O^T[dim 16nt + 4g + i][head n] -------------------------------
+      // The two transpose reads of value tile nt+1 are issued before the MFMAs
+      // of tile nt.
+      s16x4_t vb[kMlaVPf + 1][2];
+      const char* tb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tb[j] = st + troff(j);
+      auto vread = [&](int nt, s16x4_t* dst2) {
+        const char* a1 = tb[nt & 7] + 256 * (nt >> 3);
+        dst2[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
+        dst2[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1 + 16 * kMlaLatBytes));
+      };
+#pragma unroll
+      for (int j = 0; j < kMlaVPf; ++j) vread(j, vb[j]);
 #pragma unroll
       for (int nt = 0; nt < kMlaDvTiles; ++nt) {
-        const int chunk = (2 * nt + (tr_j >> 1)) ^ sw_tr;
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr0 + 16 * chunk));
-        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tr1 + 16 * chunk));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[0], o[0][nt], 0, 0, 0);
-        o[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[1], o[1][nt], 0, 0, 0);
+        if (nt + kMlaVPf < kMlaDvTiles) vread(nt + kMlaVPf, vb[(nt + kMlaVPf) % (kMlaVPf + 1)]);
+        const int cb = nt % (kMlaVPf + 1);
+        const bf16x8_t a =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vb[cb][0], vb[cb][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int hh = 0; hh < kMlaHT; ++hh)
+          o[hh][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[hh], o[hh][nt], 0, 0, 0);
       }
       stage = stage == kMlaStages - 1 ? 0 : stage + 1;
     }
 
-    // ---- replay vote (block-uniform) ----------------------------------------
+    // ---- replay vote (block-uniform) ------------------------------------------
     const int wave_bad = __any(bad) ? 1 : 0;  // every lane takes part in the wave vote
-    if (lane == 0) votes[wave] = wave_bad;
+    if (lane == 0) *reinterpret_cast<int*>(qrope + wave * kMlaQRopeWaveBytes) = wave_bad;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the vote is in LDS before the barrier
     block_sync();
-    const bool replay = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < kMlaWaves; ++w) any_bad |= *reinterpret_cast<const int*>(qrope + w * kMlaQRopeWaveBytes);
     block_sync();  // every wave has read the votes before they are written again
-    if (replay) {
+    if (any_bad) {
       wait_vmcnt<0>();
       block_sync();
       tile = piece_tile0;
@@ -314,25 +393,24 @@ mla_attn_kernel(AttnParams p, int workers) {
       pf_t = piece_tile0;
       pf_u = piece_u0;
       stage = 0;
-      issue(0);
-      if (tile + 1 < wend) issue(1);
-      m_hint[0] = m_seen[0];
-      m_hint[1] = m_seen[1];
+      for (int j = 0; j < kMlaStages - 1 && tile + j < wend; ++j) issue(j);
+#pragma unroll
+      for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = m_seen[hh];
       continue;
     }
-    m_hint[0] = -INFINITY;
-    m_hint[1] = -INFINITY;
+#pragma unroll
+    for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = -INFINITY;
 
-    // ---- piece end ------------------------------------------------------------
+    // ---- piece end --------------------------------------------------------------
     const bool whole = (lt_lo == 0) && (lt_hi == uend - ubeg);
     const int which = (lt_lo == 0) ? 1 : 0;  // 0: the unit began before this worker
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kMlaHT; ++hh) {
       float lt_ = l[hh] + __shfl_xor(l[hh], 16, 64);
       lt_ += __shfl_xor(lt_, 32, 64);
       float et = e[hh] + __shfl_xor(e[hh], 16, 64);
       et += __shfl_xor(et, 32, 64);
-      const int head = 32 * wave + 16 * hh + n;
+      const int head = kMlaHeadsPerWave * wave + 16 * hh + n;
       if (whole) {
         const int64_t row = cur_u * kMlaHeads + head;
         float* dst = p.out_o + row * kMlaDv + 4 * g;
@@ -341,7 +419,8 @@ mla_attn_kernel(AttnParams p, int workers) {
         for (int nt = 0; nt < kMlaDvTiles; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt) = o[hh][nt] * inv;
         if (g == 0) p.out_lse[row] = (m_ref[hh] + __log2f(et)) * DCP_LN2;
       } else {
-        float* dst = ws.part + ((static_cast<int64_t>(worker) * 2 + which) * kMlaHeads + head) * (kMlaDv + kPartExtra);
+        float* dst =
+            ws.part + ((static_cast<int64_t>(worker) * 2 + which) * kMlaHeads + head) * (kMlaDv + kPartExtra);
 #pragma unroll
         for (int nt = 0; nt < kMlaDvTiles; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt + 4 * g) = o[hh][nt];
         if (g == 0) {
@@ -367,6 +446,7 @@ bool mla_supported(const AttnParams& p) {
   for (int i = 0; i < 4; ++i)
     if ((kv.k_stride[i] * 2) % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(kv.k) % 16) return false;
+  if (static_cast<int64_t>(p.rank_count) * p.batch >= (int64_t(1) << 31)) return false;
   return true;
 }
 
