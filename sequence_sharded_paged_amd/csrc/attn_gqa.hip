@@ -8,13 +8,15 @@
 // one KV head).
 //
 // Work split: stream-K over (rank, request, KV head) units (splitkv.h) with
-// one persistent wavefront per worker and tiles of TOK tokens.
+// one persistent wavefront per worker and tiles of TOK tokens (16 KB of K and
+// V per tile), streamed two tiles at a time straight into registers.
 //
 // Per wavefront and tile, with lane l = 16*qd + n (n = l % 16, qd = l / 16):
 //   scores  S^T[token, head] = K[token, :] . Q[head, :]   (MFMA 16x16x32 bf16,
 //           A = K rows loaded straight from HBM in operand layout, B = Q^T
 //           held in registers, head columns >= group are zero)
-//   softmax online, per head column: running max and sums; the weights are
+//   softmax online, per head column, against a reference max that moves
+//           only when a tile's max exceeds it by more than 2^8; the weights are
 //           rounded to bf16 for the value product and the same rounded values
 //           form the normalising sum (O is an exact convex combination of the
 //           values), while an fp32 sum of the unrounded weights gives the LSE
@@ -33,6 +35,7 @@ namespace dcp {
 constexpr int kGqaDim = 128;
 constexpr int kGqaMaxWorkers = 8192;
 constexpr int kGqaWavesPerBlock = 4;
+constexpr float kGqaRescaleLog2 = 8.f;  // largest weight kept without rescaling: 2^8
 
 template <bool kFp8>
 struct GqaTile {
@@ -53,6 +56,12 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
 
 __device__ __forceinline__ u32x4_t ldg16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// KV is streamed exactly once: non-temporal loads (measured ~14% more read
+// bandwidth than cached loads on MI355X).
+__device__ __forceinline__ u32x4_t ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // Zero bytes [keep, 16) of a 16-byte vector.
 __device__ __forceinline__ u32x4_t keep_bytes(u32x4_t v, int keep) {
 #pragma unroll
@@ -65,14 +74,182 @@ __device__ __forceinline__ u32x4_t keep_bytes(u32x4_t v, int keep) {
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: one persistent wavefront per worker.
+// Tile pieces. Lane l = 16*qd + n. Tiles start at multiples of TOK and the
+// block size is a multiple of 16, so every aligned 16-token chunk lies in one
+// KV block. A lane's K rows all lie in chunk kc, its V run in chunk vc.
 // ---------------------------------------------------------------------------
 template <bool kFp8>
-__global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnParams p, int workers) {
+struct GqaLane {
   using C = GqaTile<kFp8>;
-  constexpr int TOK = C::TOK, NT = C::NT, RUN = C::RUN;
+  static __device__ __forceinline__ int kc(int n) { return (C::RUN * (n >> 2)) >> 4; }
+  static __device__ __forceinline__ int koff(int n) { return ((C::RUN * (n >> 2)) & 15) + (n & 3); }
+  static __device__ __forceinline__ int vc(int qd) { return (C::RUN * qd) >> 4; }
+  static __device__ __forceinline__ int voff(int qd) { return (C::RUN * qd) & 15; }
+};
+
+// First token of a lane's chunk in tile t; a chunk past the shard's end
+// (len) is replaced by the tile's first chunk, which always holds a token.
+template <bool kFp8>
+__device__ __forceinline__ int gqa_chunk_start(int t, int chunk, int len) {
+  const int t0 = t * GqaTile<kFp8>::TOK;
+  const int cs = t0 + 16 * chunk;
+  return cs < len ? cs : t0;
+}
+
+struct GqaIds {
+  int32_t k, v;  // physical blocks of the lane's K chunk and V chunk
+};
+
+template <bool kFp8>
+__device__ __forceinline__ GqaIds gqa_load_ids(const int32_t* bt, int t, int len, int bs, int n, int qd) {
+  using L = GqaLane<kFp8>;
+  GqaIds r;
+  r.k = bt[gqa_chunk_start<kFp8>(t, L::kc(n), len) / bs];
+  r.v = bt[gqa_chunk_start<kFp8>(t, L::vc(qd), len) / bs];
+  return r;
+}
+
+template <bool kFp8>
+struct GqaBuf {
+  u32x4_t k[GqaTile<kFp8>::NT][kFp8 ? 2 : 4];  // K rows in MFMA A-operand layout
+  u32x4_t v[8];                                // V^T runs, one per 16 value dims
+};
+
+// Issue the loads of tile t (raw bytes; masking happens in gqa_tile).
+template <bool kFp8>
+__device__ __forceinline__ void gqa_issue(GqaBuf<kFp8>& B, GqaIds ids, int t, int len, int bs, const char* kh,
+                                          int64_t ks1, int64_t ks3, const char* vh, int64_t vs1, int64_t vs4,
+                                          int n, int qd) {
+  using L = GqaLane<kFp8>;
+  constexpr int EB = kFp8 ? 1 : 2;
+  const int csk = gqa_chunk_start<kFp8>(t, L::kc(n), len);
+  const char* krow = kh + (static_cast<int64_t>(ids.k) * ks1 + static_cast<int64_t>(csk % bs + L::koff(n)) * ks3) * EB +
+                     16 * qd;
+#pragma unroll
+  for (int ut = 0; ut < GqaTile<kFp8>::NT; ++ut)
+#pragma unroll
+    for (int j = 0; j < (kFp8 ? 2 : 4); ++j) B.k[ut][j] = ldg16_stream(krow + (4 * ut) * ks3 * EB + 64 * j);
+  const int csv = gqa_chunk_start<kFp8>(t, L::vc(qd), len);
+  const char* run = vh + (static_cast<int64_t>(ids.v) * vs1 + csv % bs + L::voff(qd) + n * vs4) * EB;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) B.v[nt] = ldg16_stream(run + static_cast<int64_t>(16 * nt) * vs4 * EB);
+  // nothing of the tile computed next may move above these loads: the wait
+  // for that tile's data must leave this tile's loads in flight
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scores, online softmax and value product of one tile whose loads landed.
+template <bool kFp8>
+__device__ __forceinline__ void gqa_tile(GqaBuf<kFp8>& B, int t0, int len, float c2, const bf16x8_t (&qop)[4],
+                                         f32x4_t (&o)[8], float& m_run, float& l_run, float& e_run, int qd) {
+  using C = GqaTile<kFp8>;
+  constexpr int NT = C::NT, RUN = C::RUN;
+  constexpr int EB = kFp8 ? 1 : 2;
+  // ---- scores ---------------------------------------------------------
+  f32x4_t s[NT];
+#pragma unroll
+  for (int ut = 0; ut < NT; ++ut) {
+    s[ut] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bf16x8_t a;
+      if constexpr (kFp8) {
+        const u32x4_t& w = B.k[ut][k >> 1];
+        a = (k & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
+      } else {
+        a = __builtin_bit_cast(bf16x8_t, B.k[ut][k]);
+      }
+      s[ut] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[k], s[ut], 0, 0, 0);
+    }
+    // keep each row tile's widened operands next to their MFMAs (otherwise
+    // the scheduler hoists every conversion and doubles the live registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- online softmax (log2 domain) ----------------------------------
+#pragma unroll
+  for (int ut = 0; ut < NT; ++ut) s[ut] *= c2;
+  if (t0 + C::TOK > len) {  // last tile of the shard (wave-uniform test)
+#pragma unroll
+    for (int ut = 0; ut < NT; ++ut)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + RUN * qd + 4 * ut + i >= len) s[ut][i] = -INFINITY;
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int ut = 0; ut < NT; ++ut)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[ut][i]);
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+  // Lazy rescaling: the weights are taken relative to a reference max m_run
+  // that only moves (rescaling O and the sums) when some column's tile max
+  // exceeds it by more than 2^8; otherwise weights up to 2^8 are exact
+  // enough in fp32 and bf16 alike. The decision is wave-uniform.
+  if (__builtin_amdgcn_ballot_w64(mloc > m_run + kGqaRescaleLog2) != 0) {
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    m_run = m_new;
+    l_run *= alpha;
+    e_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+  }
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  __bf16 pb[NT][4];
+  float psum = 0.f, esum = 0.f;
+#pragma unroll
+  for (int ut = 0; ut < NT; ++ut)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = exp2f(s[ut][i] - m_use);
+      const __bf16 eb = static_cast<__bf16>(e);
+      pb[ut][i] = eb;
+      psum += static_cast<float>(eb);
+      esum += e;
+    }
+  l_run += psum;
+  e_run += esum;
+  // ---- values: V^T runs past the shard's end are zeroed (weights there
+  // are 0, but the bytes may hold anything, NaN included). Only the last
+  // tile of a shard can hold such runs; the test is wave-uniform. ---------
+  if (t0 + C::TOK > len) {
+    const int keep = (len - (t0 + RUN * qd)) * EB;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) B.v[nt] = keep_bytes(B.v[nt], keep);
+  }
+#pragma unroll
+  for (int ksx = 0; ksx < C::KS; ++ksx) {
+    const bf16x8_t pop = {pb[2 * ksx][0], pb[2 * ksx][1], pb[2 * ksx][2], pb[2 * ksx][3],
+                          pb[2 * ksx + 1][0], pb[2 * ksx + 1][1], pb[2 * ksx + 1][2], pb[2 * ksx + 1][3]};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      bf16x8_t a;
+      if constexpr (kFp8) {
+        a = ksx ? fp8x8_to_bf16x8(B.v[nt][2], B.v[nt][3]) : fp8x8_to_bf16x8(B.v[nt][0], B.v[nt][1]);
+      } else {
+        a = __builtin_bit_cast(bf16x8_t, B.v[nt]);
+      }
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, o[nt], 0, 0, 0);
+      if (nt & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel: one persistent wavefront per worker.
+// ---------------------------------------------------------------------------
+// Waves per SIMD the register allocation must allow (measured best: two
+// for fp8, whose tile work is heavier; one for bf16).
+template <bool kFp8>
+__global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
+    __attribute__((amdgpu_waves_per_eu(kFp8 ? 2 : 1))) gqa_attn_kernel(AttnParams p, int workers) {
+  using C = GqaTile<kFp8>;
+  constexpr int TOK = C::TOK;
   const int lane = threadIdx.x & 63;
-  const int worker = blockIdx.x * kGqaWavesPerBlock + (threadIdx.x >> 6);
+  // wave-uniform (the compiler cannot tell on its own): keeps every unit and
+  // tile quantity in scalar registers and the tile loop free of exec masks
+  const int worker = __builtin_amdgcn_readfirstlane(blockIdx.x * kGqaWavesPerBlock + (threadIdx.x >> 6));
   const int n = lane & 15, qd = lane >> 4;
   const int Hkv = p.kv.num_kv_heads, G = p.group;
   const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
@@ -113,11 +290,12 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnPa
     {
       const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
                              (static_cast<int64_t>(b) * p.num_q_heads + h * G + n) * kGqaDim;
+      const uint16_t* qsrc = n < G ? qrow : reinterpret_cast<const uint16_t*>(p.q);  // in bounds, then zeroed
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int d0 = kFp8 ? (64 * (k >> 1) + 16 * qd + 8 * (k & 1)) : (32 * k + 8 * qd);
-        u32x4_t raw = {0u, 0u, 0u, 0u};
-        if (n < G) raw = ldg16(qrow + d0);
+        u32x4_t raw = ldg16(qsrc + d0);
+        if (n >= G) raw = u32x4_t{0u, 0u, 0u, 0u};
         qop[k] = __builtin_bit_cast(bf16x8_t, raw);
       }
     }
@@ -130,107 +308,26 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock) gqa_attn_kernel(AttnPa
     // weights and gives the LSE.
     float m_run = -INFINITY, l_run = 0.f, e_run = 0.f;
 
-    for (int64_t t = t_lo; t < t_hi; ++t) {
-      const int t0 = static_cast<int>(t * TOK);
-      // ---- loads: K rows in operand layout, V^T runs --------------------
-      u32x4_t kraw[NT][kFp8 ? 2 : 4];
-#pragma unroll
-      for (int ut = 0; ut < NT; ++ut) {
-        const int tok = t0 + RUN * (n >> 2) + 4 * ut + (n & 3);
-        if (tok < len) {
-          const int64_t phys = bt[tok / bs];
-          const char* row = kh + (phys * ks1 + static_cast<int64_t>(tok % bs) * ks3) * EB;
-#pragma unroll
-          for (int j = 0; j < (kFp8 ? 2 : 4); ++j)
-            kraw[ut][j] = ldg16(row + (kFp8 ? (16 * qd + 64 * j) : (16 * qd + 64 * j)));
-        } else {
-#pragma unroll
-          for (int j = 0; j < (kFp8 ? 2 : 4); ++j) kraw[ut][j] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-      u32x4_t vraw[8];
-      {
-        const int tok = t0 + RUN * qd;
-        if (tok < len) {
-          const int64_t phys = bt[tok / bs];
-          const char* run = vh + (phys * vs1 + static_cast<int64_t>(tok % bs)) * EB;
-          const int keep = (len - tok) * EB;
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            u32x4_t v = ldg16(run + static_cast<int64_t>(16 * nt + n) * vs4 * EB);
-            vraw[nt] = keep < 16 ? keep_bytes(v, keep) : v;
-          }
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) vraw[nt] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-      // ---- scores ---------------------------------------------------------
-      f32x4_t s[NT];
-#pragma unroll
-      for (int ut = 0; ut < NT; ++ut) {
-        s[ut] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          bf16x8_t a;
-          if constexpr (kFp8) {
-            const u32x4_t& w = kraw[ut][k >> 1];
-            a = (k & 1) ? fp8x8_to_bf16x8(w[2], w[3]) : fp8x8_to_bf16x8(w[0], w[1]);
-          } else {
-            a = __builtin_bit_cast(bf16x8_t, kraw[ut][k]);
-          }
-          s[ut] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[k], s[ut], 0, 0, 0);
-        }
-      }
-      // ---- online softmax (log2 domain) ----------------------------------
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int ut = 0; ut < NT; ++ut)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = t0 + RUN * qd + 4 * ut + i;
-          const float x = tok < len ? s[ut][i] * c2 : -INFINITY;
-          s[ut][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
-      __bf16 pb[NT][4];
-      float psum = 0.f, esum = 0.f;
-#pragma unroll
-      for (int ut = 0; ut < NT; ++ut)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = exp2f(s[ut][i] - m_use);
-          const __bf16 eb = static_cast<__bf16>(e);
-          pb[ut][i] = eb;
-          psum += static_cast<float>(eb);
-          esum += e;
-        }
-      l_run = l_run * alpha + psum;
-      e_run = e_run * alpha + esum;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
-      // ---- values ---------------------------------------------------------
-#pragma unroll
-      for (int ksx = 0; ksx < C::KS; ++ksx) {
-        const bf16x8_t pop = {pb[2 * ksx][0], pb[2 * ksx][1], pb[2 * ksx][2], pb[2 * ksx][3],
-                              pb[2 * ksx + 1][0], pb[2 * ksx + 1][1], pb[2 * ksx + 1][2], pb[2 * ksx + 1][3]};
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          bf16x8_t a;
-          if constexpr (kFp8) {
-            a = ksx ? fp8x8_to_bf16x8(vraw[nt][2], vraw[nt][3]) : fp8x8_to_bf16x8(vraw[nt][0], vraw[nt][1]);
-          } else {
-            a = __builtin_bit_cast(bf16x8_t, vraw[nt]);
-          }
-          o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, o[nt], 0, 0, 0);
-        }
-      }
+    // Two tiles per iteration: the loads of both (32 KB per wave) are issued
+    // before either is consumed, and the block ids of the next pair are
+    // fetched meanwhile, so a wave never waits on a block-table read. Loads
+    // are unconditional (no divergent branches around them, which would make
+    // the compiler wait for every load in flight): rows past the shard's end
+    // read the tile's first chunk instead and are masked afterwards, and the
+    // second tile of the last pair, when the piece has an odd tile count,
+    // re-reads the last tile and is dropped.
+    // (tile indices inside one unit fit in 32 bits: a shard holds < 2^31 tokens)
+    const int tb = static_cast<int>(t_lo), te = static_cast<int>(t_hi), t_last = te - 1;
+    GqaIds ids_a = gqa_load_ids<kFp8>(bt, tb, len, bs, n, qd);
+    GqaIds ids_b = gqa_load_ids<kFp8>(bt, min(tb + 1, t_last), len, bs, n, qd);
+    GqaBuf<kFp8> buf_a, buf_b;
+    for (int t = tb; t < te; t += 2) {
+      gqa_issue<kFp8>(buf_a, ids_a, t, len, bs, kh, ks1, ks3, vh, vs1, vs4, n, qd);
+      gqa_issue<kFp8>(buf_b, ids_b, min(t + 1, t_last), len, bs, kh, ks1, ks3, vh, vs1, vs4, n, qd);
+      ids_a = gqa_load_ids<kFp8>(bt, min(t + 2, t_last), len, bs, n, qd);
+      ids_b = gqa_load_ids<kFp8>(bt, min(t + 3, t_last), len, bs, n, qd);
+      gqa_tile<kFp8>(buf_a, t * TOK, len, c2, qop, o, m_run, l_run, e_run, qd);
+      if (t + 1 < te) gqa_tile<kFp8>(buf_b, (t + 1) * TOK, len, c2, qop, o, m_run, l_run, e_run, qd);
     }
 
     // ---- piece end: full unit -> final output, else partial --------------
