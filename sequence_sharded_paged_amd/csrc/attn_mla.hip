@@ -8,28 +8,39 @@
 // Parallel (DCP)" (vLLM Ascend design doc), section "Decode" (attention
 // against the local KV shard, partial output and LSE out).
 //
+// At 128 heads a token costs 2 x 128 x (576 + 512) flops for 1152 bytes, so
+// at the HBM rate this kernel needs most of the chip's bf16 MFMA rate: the
+// design goal is to keep the matrix cores busy, and everything else (LDS
+// operand reads, softmax, address arithmetic) runs in their shadow.
+//
 // Work split: stream-K over (rank, request) units (splitkv.h), one persistent
-// 256-thread workgroup per worker, tiles of 32 tokens. Per workgroup:
-//   * a 3-stage LDS ring of 32-token tiles (36 KB each) is filled straight
-//     from HBM with global_load_lds_dwordx4; the 16-byte chunks of a row are
-//     XOR-swizzled by the row index so the MFMA operand reads spread over the
-//     LDS banks. Waits are explicit vmcnt counts plus raw s_barrier, so two
-//     tiles stay in flight while the third is consumed;
-//   * each of the 4 wavefronts owns 32 query heads: its Q (32 x 576 bf16, 144
-//     VGPRs) and its O accumulator (32 x 512 fp32, 256 AGPRs) stay in
-//     registers for the whole piece;
+// 256-thread workgroup (one wavefront per SIMD) per worker, tiles of 32
+// tokens. Per workgroup:
+//   * a 4-stage LDS ring of 32-token tiles (36 KB each) is filled straight
+//     from HBM with global_load_lds_dwordx4 (each wavefront loads 8 of the 32
+//     rows); the 16-byte chunks of a row are XOR-swizzled by the row index so
+//     that the MFMA operand reads spread over the LDS banks. A tile is
+//     refilled four tiles ahead, right after the barrier that ends the last
+//     read of its stage, so two to three tiles are always in flight;
+//   * each of the 4 wavefronts owns 32 query heads: its latent Q (32 x 512
+//     bf16, 128 VGPRs) and its O accumulator (32 x 512 fp32, 256 AGPRs) stay
+//     in registers for the whole piece; the rope part of Q sits in LDS;
 //   * scores S^T[token, head] = K[token, :] . Q[head, :] on 16x16x32 bf16
 //     MFMA, K rows read from LDS with ds_read_b128 (one read feeds both head
 //     tiles);
 //   * softmax weights in log2 units relative to a per-piece reference max
-//     (no rescaling of the 256-register accumulator inside the loop; a piece
-//     whose scores outgrow the reference by more than 2^64 is replayed with a
-//     higher reference), rounded to bf16 for the value product, with an fp32
-//     sum for the LSE (as in the GQA kernel);
+//     (the first tile's): no rescaling of the 256-register accumulator and no
+//     cross-lane reduction inside the loop; a piece whose scores outgrow the
+//     reference by more than 2^64 is replayed with a higher reference. The
+//     weights are rounded to bf16 for the value product and their sum (the
+//     normaliser) is taken over the same rounded values, with an fp32 sum of
+//     the unrounded weights for the LSE (as in the GQA kernel);
 //   * values O^T[dim, head] += V^T[dim, token] . P^T[token, head]; V^T comes
 //     from the same LDS rows through ds_read_b64_tr_b16, whose 16-lane
-//     transpose hands each lane four consecutive tokens of one dimension, so
-//     no second copy of the tile is needed.
+//     transpose hands each lane four consecutive tokens of one dimension;
+//   * software pipeline across tiles: the softmax of tile t is interleaved,
+//     one weight per k-step, with the score MFMAs of tile t+1, and the value
+//     MFMAs of tile t follow, so the matrix core never waits for the softmax.
 #include "splitkv.h"
 
 namespace dcp {
@@ -38,44 +49,35 @@ constexpr int kMlaDk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaHeads = 128;
 constexpr int kMlaTile = 32;                                     // tokens per tile
-#ifndef DCP_MLA_STAGES
-#define DCP_MLA_STAGES 4
-#endif
-constexpr int kMlaStages = DCP_MLA_STAGES;                       // LDS ring depth (tiles in flight + 1)
+constexpr int kMlaStages = 4;                                    // LDS ring depth
 constexpr int kMlaRowBytes = kMlaDk * 2;                         // 1152
 constexpr int kMlaStageBytes = kMlaTile * kMlaRowBytes;          // 36864
 constexpr int kMlaLatBytes = kMlaDv * 2;                         // 1024: latent part of a row (also V)
 constexpr int kMlaRopeOff = kMlaTile * kMlaLatBytes;             // 32768: rope rows follow the latent rows
 constexpr int kMlaRopeBytes = kMlaRowBytes - kMlaLatBytes;       // 128
-#ifndef DCP_MLA_WAVES
-#define DCP_MLA_WAVES 4
-#endif
-constexpr int kMlaWaves = DCP_MLA_WAVES;                         // wavefronts per workgroup (4 or 8)
+constexpr int kMlaWaves = 4;                                     // wavefronts per workgroup
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32 or 16
-constexpr int kMlaHT = kMlaHeadsPerWave / 16;                    // 16-head MFMA tiles per wavefront
-constexpr int kMlaLatRowsPerWave = kMlaTile / kMlaWaves;         // latent rows loaded per wave and tile
+constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32
+constexpr int kMlaHT = kMlaHeadsPerWave / 16;                    // 2 16-head MFMA tiles per wavefront
+constexpr int kMlaRowsPerWave = kMlaTile / kMlaWaves;            // 8 rows of a tile loaded per wavefront
+constexpr int kMlaDmaPerTile = kMlaRowsPerWave + 1;              // DMA instructions per wavefront and tile
 constexpr int kMlaKSteps = kMlaDk / 32;                          // 18
-#ifndef DCP_MLA_QREG
-#define DCP_MLA_QREG 16
-#endif
+constexpr int kMlaKStepsLat = kMlaDv / 32;                       // 16: latent k-steps (Q in VGPRs)
+constexpr int kMlaQRopeWaveBytes = kMlaHT * (kMlaKSteps - kMlaKStepsLat) * 64 * 16;  // 4 KB per wave
+constexpr int kMlaDvTiles = kMlaDv / 16;                         // 32
 #ifndef DCP_MLA_KPF
-#define DCP_MLA_KPF 1
+#define DCP_MLA_KPF 3
 #endif
 #ifndef DCP_MLA_VPF
-#define DCP_MLA_VPF 1
+#define DCP_MLA_VPF 3
 #endif
-constexpr int kMlaKStepsReg = DCP_MLA_QREG;                      // k-steps of Q kept in VGPRs; the rest in LDS
-constexpr int kMlaKPf = DCP_MLA_KPF;                             // score-operand read distance (k-steps)
-constexpr int kMlaVPf = DCP_MLA_VPF;                             // value-operand read distance (tiles)
-constexpr int kMlaQLdsSteps = kMlaKSteps - kMlaKStepsReg;        // k-steps of Q held in LDS
-constexpr int kMlaQRopeWaveBytes = kMlaHT * kMlaQLdsSteps * 64 * 16;  // per wave
-constexpr int kMlaDvTiles = kMlaDv / 16;                         // 32
+constexpr int kMlaKPf = DCP_MLA_KPF;  // score-operand read distance (k-steps)
+constexpr int kMlaVPf = DCP_MLA_VPF;  // value-operand read distance (value tiles)
 constexpr int kMlaMaxWorkers = 512;
-constexpr float kMlaRefSlack = 64.f;  // log2 units a tile max may exceed the piece's reference
+constexpr float kMlaRefSlack = 64.f;  // log2 units a score may exceed the piece's reference
 
-static_assert(kMlaWaves == 4 || kMlaWaves == 8, "4 or 8 wavefronts");
-static_assert(kMlaKStepsReg % 4 == 0 && kMlaKStepsReg <= 16, "latent k-steps in registers");
+static_assert(kMlaStages == 4, "the refill distance below assumes 4 stages");
+static_assert(kMlaKStepsLat == 16 && kMlaKSteps - kMlaKStepsLat == 2, "16 latent + 2 rope k-steps");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -102,6 +104,21 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
 }
 
+// Same, from a wave-uniform base plus a 32-bit per-lane byte offset.
+// (The base and M0 values are wave-uniform by construction; readfirstlane
+// pins them to SGPRs where the compiler cannot prove it.)
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  // (readfirstlane yields a signed int: each half is taken as uint32_t before
+  // widening, or a low word with bit 31 set would smear into the high word)
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  const uint64_t bu = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(bu)), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every tile in flight); the asm memory clobber keeps the compiler
 // from moving LDS accesses across it.
@@ -111,23 +128,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-// Chunk swizzles. A latent row holds 64 16-byte chunks; chunk c of row r sits
-// at slot c ^ lat_swz(r). lat_swz is a bijection of r & 15 whose bits 1..3
-// carry r & 7: the 16 rows of a score-operand read (same chunk) land on 16
-// distinct slots mod 16, and the 4 rows x 2 chunks of a transpose read as
-// well. Rope rows (8 chunks) use chunk ^ (r & 7).
-__device__ __forceinline__ int lat_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ int rope_swz(int row) { return row & 7; }
 
-__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads),
-                               amdgpu_waves_per_eu(kMlaWaves / 4, kMlaWaves / 4)))
+// s_waitcnt lgkmcnt(0) with vmcnt / expcnt left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// bf16 pair (round to nearest even) packed in one dword, low half first.
+__device__ __forceinline__ bf16x2_t pack_bf16(float lo, float hi) {
+  return bf16x2_t{static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+}
+
+// LDS tile layout, in MFMA operand order. The tile's 32 rows x 72 chunks of
+// 16 bytes form 36 blocks of 1 KB, block 2 ks + u holding chunks 4 ks .. 4 ks
+// + 3 of rows 16 u .. 16 u + 15 (the score operand of k-step ks for token
+// half u): chunk 4 ks + c of row 16 u + r sits at 16 (16 c + (r ^ 4 c)) in
+// its block. A score-operand read (lane 16 c + r) is then one contiguous
+// 1 KB block, and a transpose read of the value operand (4 rows x 2 chunks
+// per 16 lanes) touches two 64-byte runs in different bank halves.
+__device__ __forceinline__ int mla_slot(int r, int c) { return 16 * c + (r ^ (4 * c)); }
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads), amdgpu_waves_per_eu(1, 1)))
 mla_attn_kernel(AttnParams p, int workers) {
   __shared__ __attribute__((aligned(16))) char lds[kMlaStages * kMlaStageBytes];
-  // rope part of Q in operand order: [wave][ks - 16][lane] x 16 bytes
-  __shared__ __attribute__((aligned(16))) char qrope[kMlaWaves * kMlaQRopeWaveBytes];
-  // The replay vote of wave w lives in the first 4 bytes of w's own Q slice:
-  // by the time a wave votes it no longer reads its slice, and the slice is
+  // rope part of Q in operand order: [wave][hh][ks - 16][lane] x 16 bytes.
+  // The replay vote of wave w lives in the first 4 bytes of w's own slice: by
+  // the time a wave votes it no longer reads its slice, and the slice is
   // refilled only after every wave has read the votes.
+  __shared__ __attribute__((aligned(16))) char qrope[kMlaWaves * kMlaQRopeWaveBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int n = lane & 15, g = lane >> 4;
@@ -143,80 +169,178 @@ mla_attn_kernel(AttnParams p, int workers) {
 
   const int bs = p.kv.block_size;
   const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks3 = p.kv.k_stride[3];
+  const int row_bytes = static_cast<int>(ks3 * 2);  // bytes between consecutive tokens of a block
   const char* kbase = static_cast<const char*>(p.kv.k);
   const float c2 = p.softmax_scale * DCP_LOG2E;
-  const bool rope_loader = wave < 4;   // waves 0..3 also load the rope rows (8 rows each)
-  (void)rope_loader;
+  const uint32_t lds0 = lds_addr(lds);
+  auto stage_of = [&](int64_t t) __attribute__((always_inline)) {
+    return static_cast<int>((t - wstart) & (kMlaStages - 1));
+  };
 
-  // ---- tile prefetch (uniform control flow) --------------------------------
-  int64_t pf_u = ld_uniform(ws.wunit + worker);
-  int64_t pf_t = wstart;
-  auto issue = [&](int stage) {
-    while (ld_uniform(ws.prefix + pf_u + 1) <= pf_t) ++pf_u;
-    const int lt = static_cast<int>(pf_t - ld_uniform(ws.prefix + pf_u));
-    const int uu = static_cast<int>(pf_u);
-    const int b = uu % p.batch, r = uu / p.batch;
-    const int len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r);
-    const int t0 = lt * kMlaTile;
-    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-    // tokens t0..t0+15 share one block and so do t0+16..t0+31 (block_size %
-    // 16 == 0); a row past the end re-reads token t0 (finite data, zero weight)
-    const int vb_a = t0 / bs, off_a = t0 - vb_a * bs;
-    const bool has_b = t0 + 16 < len;
-    const int vb_b = has_b ? (t0 + 16) / bs : vb_a;
-    const int off_b = has_b ? t0 + 16 - vb_b * bs : off_a;
-    const int64_t base_a = ld_uniform(bt + vb_a) * ks1 + static_cast<int64_t>(off_a) * ks3;
-    const int64_t base_b = ld_uniform(bt + vb_b) * ks1 + static_cast<int64_t>(off_b) * ks3;
-    const char* rank_k = kbase + r * ks0 * 2;
-    char* dst = lds + stage * kMlaStageBytes;
-    // latent rows: one row per instruction (uniform address), lane = destination slot
+  // ---- tile sources -----------------------------------------------------------
+  // A walker over the worker's tiles in order: per unit it caches the length,
+  // block-table row and rank base; per tile it advances the (virtual block,
+  // offset) of the tile's first token and yields the two 16-token halves
+  // (tokens t0 .. t0+15 share one block and so do t0+16 .. t0+31, block_size %
+  // 16 == 0). Rows past the shard's end are replaced by the last valid row
+  // of their half, or of the first half if the second has none (finite data,
+  // zero weight): nv0 / nv1 give the rows to clamp to, and base1 = base0 when
+  // the second half is empty.
+  struct Walker {
+    int64_t t, u, ubeg, uend;
+    bool fresh;
+    int len, vb, off;
+    const int32_t* bt;
+    const char* rk;
+  };
+  struct TileSrc {
+    const char* base0;
+    const char* base1;
+    int nv0, nv1;
+  };
+  auto walker_at = [&](int64_t t, int64_t u) __attribute__((always_inline)) {
+    Walker w;
+    w.t = t;
+    w.u = u;
+    w.ubeg = ld_uniform(ws.prefix + u);
+    w.uend = ld_uniform(ws.prefix + u + 1);
+    w.fresh = true;
+    w.len = w.vb = w.off = 0;
+    w.bt = p.block_table;
+    w.rk = kbase;
+    return w;
+  };
+  auto next_src = [&](Walker& w) __attribute__((always_inline)) {
+    while (w.uend <= w.t) {
+      ++w.u;
+      w.ubeg = w.uend;
+      w.uend = ld_uniform(ws.prefix + w.u + 1);
+      w.fresh = true;
+    }
+    if (w.fresh) {
+      const int uu = static_cast<int>(w.u), b = uu % p.batch, r = uu / p.batch;
+      w.len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r);
+      w.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+      w.rk = kbase + r * ks0 * 2;
+      const int t0 = static_cast<int>(w.t - w.ubeg) * kMlaTile;
+      w.vb = t0 / bs;
+      w.off = t0 - w.vb * bs;
+      w.fresh = false;
+    }
+    const int t0 = static_cast<int>(w.t - w.ubeg) * kMlaTile;
+    TileSrc src;
+    src.nv0 = min(16, w.len - t0);
+    const int nv1 = min(16, w.len - t0 - 16);
+    src.base0 = w.rk + (static_cast<int64_t>(ld_uniform(w.bt + w.vb)) * ks1 + w.off * ks3) * 2;
+    src.base1 = src.base0;
+    src.nv1 = src.nv0;
+    if (nv1 > 0) {  // uniform
+      int off_b = w.off + 16, vb_b = w.vb;
+      if (off_b >= bs) { off_b -= bs; ++vb_b; }
+      src.base1 = w.rk + (static_cast<int64_t>(ld_uniform(w.bt + vb_b)) * ks1 + off_b * ks3) * 2;
+      src.nv1 = nv1;
+    }
+    ++w.t;
+    w.off += kMlaTile;
+    while (w.off >= bs) { w.off -= bs; ++w.vb; }
+    return src;
+  };
+
+  // ---- DMA producer -------------------------------------------------------------
+  // Wave w loads blocks w, w+4, .., w+32 of each tile: token half w % 2,
+  // k-steps w / 2 + 2 k (k = 0 .. 8); DMA lane 16 c + m fetches row m ^ 4 c of
+  // the half, chunk 4 ks + c. A refill (one wave's share of a tile) is
+  // prepared while the previous tile computes, and its 9 DMAs are spread
+  // over the k-steps of the next score phase.
+  Walker dw = walker_at(wstart, ld_uniform(ws.wunit + worker));
+  const int dma_row = n ^ (4 * g);
+  const int my_half = wave & 1;
+  struct Refill {
+    const char* base;  // this wave's token half
+    uint32_t voff;     // lane offset of k-step w / 2
+    uint32_t m0;       // LDS address of block w of the stage
+  };
+  auto prepare = [&]() __attribute__((always_inline)) {
+    const int stage = stage_of(dw.t);
+    const TileSrc src = next_src(dw);
+    Refill r;
+    r.base = my_half ? src.base1 : src.base0;
+    const int nv = my_half ? src.nv1 : src.nv0;
+    r.voff = static_cast<uint32_t>(min(dma_row, nv - 1) * row_bytes + 16 * g + 64 * (wave >> 1));
+    r.m0 = lds0 + stage * kMlaStageBytes + wave * 1024;
+    return r;
+  };
+  // DMA k (0 .. 8) of this wave for the refill r: k-step w / 2 + 2 k, block w + 4 k
+  auto dma = [&](const Refill& r, int k) __attribute__((always_inline)) {
+    dma16_s(r.voff + 128 * k, r.base, r.m0 + 4096 * k);
+  };
+  Refill next_refill;          // prepared refill (valid when has_next)
+  bool has_next = false;       // uniform
+  Refill pending;              // refill whose DMAs the next score phase issues
+  bool has_pending = false;    // uniform
+
+  // (Re)start the ring at tile t (unit u): load tiles t .. t+3 at once and
+  // wait until the first two have landed everywhere.
+  auto restart = [&](int64_t t, int64_t u) __attribute__((always_inline)) {
+    dw = walker_at(t, u);
+    has_next = has_pending = false;
+    for (int j = 0; j < kMlaStages && t + j < wend; ++j) {
+      const Refill r = prepare();
 #pragma unroll
-    for (int k = 0; k < kMlaLatRowsPerWave; ++k) {
-      const int row = kMlaLatRowsPerWave * wave + k;
-      const int64_t el = (t0 + row < len) ? (row < 16 ? base_a : base_b) + (row & 15) * ks3 : base_a;
-      dma16(rank_k + el * 2 + 16 * (lane ^ lat_swz(row)), lds_addr(dst + row * kMlaLatBytes));
+      for (int k = 0; k < kMlaDmaPerTile; ++k) dma(r, k);
     }
-    // rope rows 8*wave .. 8*wave+7 (waves 0..3), 8 chunks each
-    if (rope_loader) {
-      const int row = 8 * wave + (lane >> 3);
-      const int64_t el = (t0 + row < len) ? (wave < 2 ? base_a : base_b) + (row & 15) * ks3 : base_a;
-      dma16(rank_k + el * 2 + kMlaLatBytes + 16 * ((lane & 7) ^ rope_swz(row)),
-            lds_addr(dst + kMlaRopeOff + 8 * wave * kMlaRopeBytes));
-    }
-    ++pf_t;
+    const int64_t later = min<int64_t>(max<int64_t>(wend - t - 2, 0), 2);  // tiles allowed in flight
+    if (later == 2) wait_vmcnt<2 * kMlaDmaPerTile>();
+    else if (later == 1) wait_vmcnt<kMlaDmaPerTile>();
+    else wait_vmcnt<0>();
+    block_sync();
   };
-  // this thread's DMA count per tile (for the vmcnt waits)
-  // waits until this thread's loads of the current tile have landed; `ahead`
-  // younger tiles (0 .. stages-2) may stay in flight
-  auto wait_tile = [&](int ahead) {
-    constexpr int a = kMlaLatRowsPerWave + 1, b = kMlaLatRowsPerWave;
-    if (ahead <= 0) wait_vmcnt<0>();
-    else if (ahead == 1) { if (rope_loader) wait_vmcnt<a>(); else wait_vmcnt<b>(); }
-    else if (ahead == 2 || kMlaStages < 4) { if (rope_loader) wait_vmcnt<2 * a>(); else wait_vmcnt<2 * b>(); }
-    else { if (rope_loader) wait_vmcnt<3 * a>(); else wait_vmcnt<3 * b>(); }
+  // During tile t's value phase: prepare the refill with tile t+4 (issued
+  // after the barrier that ends tile t).
+  auto begin_tile = [&](int64_t t) __attribute__((always_inline)) {
+    has_next = t + kMlaStages < wend;
+    if (has_next) next_refill = prepare();
+  };
+  // End of tile t (every read of its stage issued): wait until tile t+2 has
+  // landed; the refill of t's stage with tile t+4 becomes pending. Tile t+3's
+  // DMAs were issued during this iteration's score phase (or by restart), so
+  // they are the only ones allowed to stay in flight.
+  auto end_tile = [&](int64_t t) __attribute__((always_inline)) {
+    wait_lgkm0();
+    if (t + 3 < wend) wait_vmcnt<kMlaDmaPerTile>();
+    else wait_vmcnt<0>();
+    block_sync();
+    pending = next_refill;
+    has_pending = has_next;
+  };
+  // DMA j of the pending refill, issued after k-step 2 j of a score phase
+  auto pending_dma = [&](int ks) __attribute__((always_inline)) {
+    if ((ks & 1) == 0 && ks / 2 < kMlaDmaPerTile && has_pending) dma(pending, ks / 2);
+    if (ks == 2 * (kMlaDmaPerTile - 1)) has_pending = false;
   };
 
-  for (int j = 0; j < kMlaStages - 1 && wstart + j < wend; ++j) issue(j);
+  // ---- per-lane LDS operand offsets ------------------------------------------
+  // score operand of k-step ks, token half u: row n, chunk 4 ks + g ->
+  //   koff + 2048 ks + 1024 u
+  const int koff = 16 * mla_slot(n, g);
+  // value operand of tile nt (dims 16 nt .. +15), token half u: the lane
+  // addresses row 4 g + n / 4, dims 16 nt + 4 (n % 4) .. +3, i.e. chunk
+  // 4 (nt / 2) + c with c = 2 (nt % 2) + (n % 4) / 2, byte 8 ((n % 4) % 2) ->
+  //   voff[nt % 2] + 2048 (nt / 2) + 1024 u
+  int voff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    voff[q] = 16 * mla_slot(4 * g + (n >> 2), 2 * q + ((n & 3) >> 1)) + 8 * (n & 1);
+  char* qr = qrope + wave * kMlaQRopeWaveBytes + lane * 16;
+
+  restart(wstart, ld_uniform(ws.wunit + worker));
 
   int64_t cur_u = ld_uniform(ws.wunit + worker);  // unit of the tile being computed
   int64_t tile = wstart;
-  int stage = 0;
   float m_hint[kMlaHT];  // reference for a replayed piece
+  bool replay = false;   // the current piece is a replay (at most one per piece)
 #pragma unroll
   for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = -INFINITY;
-  // per-lane LDS byte offsets (the swizzles only touch the low 4 bits of a
-  // chunk index, so the rest of each address is an immediate)
-  // score operand, k-step ks: row n, chunk (4ks + g) ^ lat_swz(n) =
-  //   koff(ks & 3) + 256 * (ks >> 2) bytes; value operand, tile nt: row tr_row,
-  //   chunk (2nt + tr_j / 2) ^ lat_swz(tr_row) = troff(nt & 7) + 256 * (nt >> 3)
-  const int kroff = kMlaRopeOff + n * kMlaRopeBytes;
-  const int tr_row = 4 * g + (n >> 2);             // LDS row (u = 0) of this lane's transpose read
-  const int tr_j = n & 3;
-  auto koff = [&](int j) { return n * kMlaLatBytes + 16 * ((4 * j + g) ^ lat_swz(n)); };
-  auto troff = [&](int j) {
-    return tr_row * kMlaLatBytes + 8 * (tr_j & 1) + 16 * ((2 * j + (tr_j >> 1)) ^ lat_swz(tr_row));
-  };
-  char* qr = qrope + wave * kMlaQRopeWaveBytes + lane * 16;
 
   while (tile < wend) {
     while (ld_uniform(ws.prefix + cur_u + 1) <= tile) ++cur_u;
@@ -225,21 +349,22 @@ mla_attn_kernel(AttnParams p, int workers) {
     const int b = static_cast<int>(cur_u % p.batch);
     const int len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin +
                                static_cast<int>(cur_u / p.batch));
+    const int64_t piece_tile0 = tile, piece_end = tile + (lt_hi - lt_lo);
 
-    // Q operand (B of the score MFMA): head 16*wave + n, dims 32*ks + 8*g .. +8;
-    // latent k-steps in VGPRs, rope k-steps in this wave's slice of LDS
-    bf16x8_t qop[kMlaHT][kMlaKStepsReg];
+    // Q operand (B of the score MFMA): head 32 wave + 16 hh + n, dims 32 ks +
+    // 8 g .. +8; latent k-steps in VGPRs, rope k-steps in this wave's slice
+    bf16x8_t qop[kMlaHT][kMlaKStepsLat];
     {
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) +
                            (static_cast<int64_t>(b) * kMlaHeads + kMlaHeadsPerWave * wave + n) * kMlaDk + 8 * g;
 #pragma unroll
       for (int hh = 0; hh < kMlaHT; ++hh) {
 #pragma unroll
-        for (int ks = 0; ks < kMlaKStepsReg; ++ks)
+        for (int ks = 0; ks < kMlaKStepsLat; ++ks)
           qop[hh][ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
 #pragma unroll
-        for (int ks = kMlaKStepsReg; ks < kMlaKSteps; ++ks)
-          *reinterpret_cast<bf16x8_t*>(qr + (hh * (kMlaKSteps - kMlaKStepsReg) + ks - kMlaKStepsReg) * 1024) =
+        for (int ks = kMlaKStepsLat; ks < kMlaKSteps; ++ks)
+          *reinterpret_cast<bf16x8_t*>(qr + (hh * (kMlaKSteps - kMlaKStepsLat) + ks - kMlaKStepsLat) * 1024) =
               *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
       }
     }
@@ -248,158 +373,194 @@ mla_attn_kernel(AttnParams p, int workers) {
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // The weights of a piece are taken relative to a fixed reference max m_ref
-    // (the first tile's max), so the accumulator is never rescaled: weights up
-    // to 2^kMlaRefSlack are exact in fp32 / bf16. If any tile's max exceeds the
-    // reference by more than that, the workgroup replays the piece with the
-    // largest max seen as the reference (m_hint).
-    const int64_t piece_tile0 = tile, piece_u0 = cur_u;
-    float m_ref[kMlaHT], m_seen[kMlaHT], l[kMlaHT], e[kMlaHT];
+    // ---- piece state ------------------------------------------------------------
+    // Weights are exp2(s c2 - m_ref) with m_ref fixed for the piece (the first
+    // tile's max unless a replay hands one in); mx tracks the largest exponent
+    // seen, for the replay vote and the next reference.
+    float m_ref[kMlaHT], mx[kMlaHT], l[kMlaHT], e[kMlaHT];
     f32x4_t o[kMlaHT][kMlaDvTiles];
 #pragma unroll
     for (int hh = 0; hh < kMlaHT; ++hh) {
       m_ref[hh] = m_hint[hh];
-      m_seen[hh] = m_hint[hh];
+      mx[hh] = -INFINITY;
       l[hh] = 0.f;
       e[hh] = 0.f;
 #pragma unroll
       for (int nt = 0; nt < kMlaDvTiles; ++nt) o[hh][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    bool bad = false;
-    for (int64_t lt = lt_lo; lt < lt_hi; ++lt, ++tile) {
-      wait_tile(static_cast<int>(min<int64_t>(wend - 1 - tile, kMlaStages - 2)));
-      block_sync();
-      if (tile + kMlaStages - 1 < wend) issue(stage == 0 ? kMlaStages - 1 : stage - 1);
-      const char* st = lds + stage * kMlaStageBytes;
+    bool need_ref = !replay;  // uniform
 
-      // ---- scores S^T[token 16u + 4g + i][head n] ----------------------------
-      // The K operand of k-step ks+1 is read before the MFMAs of step ks.
-      // per-tile operand bases; everything else of an address is an immediate
-      const char* kb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kb[j] = st + koff(j);
-      const char* krb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) krb[j] = st + kroff + 16 * ((4 * j + g) ^ rope_swz(n));
-      auto kaddr = [&](int ks, int u) -> const char* {
-        return ks < kMlaDv / 32 ? kb[ks & 3] + 256 * (ks >> 2) + u * 16 * kMlaLatBytes
-                                : krb[ks - kMlaDv / 32] + u * 16 * kMlaRopeBytes;
-      };
-      f32x4_t s[kMlaHT][2];
+    // ---- score MFMAs of one tile, with `slice(ks)` (VALU work of the previous
+    // tile) placed after the MFMAs of k-step ks -----------------------------------
+    auto scores = [&](const char* st, f32x4_t (&s)[kMlaHT][2], auto&& slice) __attribute__((always_inline)) {
 #pragma unroll
       for (int hh = 0; hh < kMlaHT; ++hh) s[hh][0] = s[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const char* kb = st + koff;
       bf16x8_t ka[kMlaKPf + 1][2];
+      auto kread = [&](int ks) __attribute__((always_inline)) {
+        ka[ks % (kMlaKPf + 1)][0] = *reinterpret_cast<const bf16x8_t*>(kb + 2048 * ks);
+        ka[ks % (kMlaKPf + 1)][1] = *reinterpret_cast<const bf16x8_t*>(kb + 2048 * ks + 1024);
+      };
 #pragma unroll
-      for (int j = 0; j < kMlaKPf; ++j) {
-        ka[j][0] = *reinterpret_cast<const bf16x8_t*>(kaddr(j, 0));
-        ka[j][1] = *reinterpret_cast<const bf16x8_t*>(kaddr(j, 1));
-      }
+      for (int j = 0; j < kMlaKPf; ++j) kread(j);
 #pragma unroll
       for (int ks = 0; ks < kMlaKSteps; ++ks) {
-        if (ks + kMlaKPf < kMlaKSteps) {
-          ka[(ks + kMlaKPf) % (kMlaKPf + 1)][0] = *reinterpret_cast<const bf16x8_t*>(kaddr(ks + kMlaKPf, 0));
-          ka[(ks + kMlaKPf) % (kMlaKPf + 1)][1] = *reinterpret_cast<const bf16x8_t*>(kaddr(ks + kMlaKPf, 1));
-        }
+        if (ks + kMlaKPf < kMlaKSteps) kread(ks + kMlaKPf);
 #pragma unroll
         for (int hh = 0; hh < kMlaHT; ++hh) {
-          const bf16x8_t bq = ks < kMlaKStepsReg
-                                  ? qop[hh][ks < kMlaKStepsReg ? ks : 0]
-                                  : *reinterpret_cast<const bf16x8_t*>(
-                                        qr + (hh * (kMlaKSteps - kMlaKStepsReg) + ks - kMlaKStepsReg) * 1024);
+          bf16x8_t bq;
+          if (ks < kMlaKStepsLat)
+            bq = qop[hh][ks < kMlaKStepsLat ? ks : 0];
+          else
+            bq = *reinterpret_cast<const bf16x8_t*>(
+                qr + (hh * (kMlaKSteps - kMlaKStepsLat) + ks - kMlaKStepsLat) * 1024);
 #pragma unroll
           for (int u = 0; u < 2; ++u)
             s[hh][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % (kMlaKPf + 1)][u], bq, s[hh][u], 0, 0, 0);
         }
+        slice(ks);
+        pending_dma(ks);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
 
-      // ---- softmax weights (log2 units, fixed reference) ----------------------
-      const int tok0 = static_cast<int>(lt) * kMlaTile + 4 * g;   // + 16u + i
-      const bool partial = static_cast<int>(lt) * kMlaTile + kMlaTile > len;   // uniform
-      bf16x8_t pop[kMlaHT];
-#pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[hh][u][i] *= c2;
-        if (partial) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (tok0 + 16 * u + i >= len) s[hh][u][i] = -INFINITY;
-        }
-        float mt = fmaxf(fmaxf(fmaxf(s[hh][0][0], s[hh][0][1]), fmaxf(s[hh][0][2], s[hh][0][3])),
-                         fmaxf(fmaxf(s[hh][1][0], s[hh][1][1]), fmaxf(s[hh][1][2], s[hh][1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        m_seen[hh] = fmaxf(m_seen[hh], mt);
-        if (m_ref[hh] == -INFINITY) m_ref[hh] = mt;
-        bad |= mt > m_ref[hh] + kMlaRefSlack;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // v_exp_f32: exact enough for weights, flushes results below 2^-126 to 0
-            const float pe = __builtin_amdgcn_exp2f(s[hh][u][i] - m_ref[hh]);
-            const __bf16 pb = static_cast<__bf16>(pe);
-            pop[hh][4 * u + i] = pb;
-            l[hh] += static_cast<float>(pb);
-            e[hh] += pe;
-          }
+    // ---- softmax of one tile: weight j of this lane (head tile j / 8, token
+    // 16 ((j / 4) % 2) + 4 g + j % 4), one per slice --------------------------------
+    f32x4_t s_cur[kMlaHT][2], s_nxt[kMlaHT][2];
+    u32x4_t pw[kMlaHT];  // packed bf16 weights: the B operand of the value MFMA
+    float pe_lo = 0.f;
+    auto weight = [&](int j) __attribute__((always_inline)) {
+      if (j >= 2 * kMlaHT * 4) return;
+      const int hh = j >> 3, u = (j >> 2) & 1, i = j & 3;
+      const float x = fmaf(s_cur[hh][u][i], c2, -m_ref[hh]);
+      mx[hh] = fmaxf(mx[hh], x);
+      const float pe = __builtin_amdgcn_exp2f(x);  // v_exp_f32; results below 2^-126 flush to 0
+      e[hh] += pe;
+      if (i & 1) {
+        const bf16x2_t pk = pack_bf16(pe_lo, pe);
+        pw[hh][2 * u + (i >> 1)] = __builtin_bit_cast(uint32_t, pk);
+        l[hh] = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{__bf16(1.f), __bf16(1.f)}, l[hh], false);
+      } else {
+        pe_lo = pe;
       }
+    };
+    auto no_slice = [](int) __attribute__((always_inline)) {};
 
-      // ---- values O^T[dim 16nt + 4g + i][head n] -------------------------------
-      // The two transpose reads of value tile nt+1 are issued before the MFMAs
-      // of tile nt.
+    // ---- value MFMAs of one tile --------------------------------------------------
+    auto values = [&](const char* st, auto&& side) __attribute__((always_inline)) {
+      const char* vbase0 = st + voff[0];
+      const char* vbase1 = st + voff[1];
       s16x4_t vb[kMlaVPf + 1][2];
-      const char* tb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tb[j] = st + troff(j);
-      auto vread = [&](int nt, s16x4_t* dst2) {
-        const char* a1 = tb[nt & 7] + 256 * (nt >> 3);
-        dst2[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
-        dst2[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1 + 16 * kMlaLatBytes));
+      auto vread = [&](int nt) __attribute__((always_inline)) {
+        const char* a1 = ((nt & 1) ? vbase1 : vbase0) + 2048 * (nt >> 1);
+        vb[nt % (kMlaVPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
+        vb[nt % (kMlaVPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1 + 1024));
       };
 #pragma unroll
-      for (int j = 0; j < kMlaVPf; ++j) vread(j, vb[j]);
+      for (int j = 0; j < kMlaVPf; ++j) vread(j);
 #pragma unroll
       for (int nt = 0; nt < kMlaDvTiles; ++nt) {
-        if (nt + kMlaVPf < kMlaDvTiles) vread(nt + kMlaVPf, vb[(nt + kMlaVPf) % (kMlaVPf + 1)]);
+        if (nt == 2) side();  // scalar work in the shadow of the MFMAs
+        if (nt + kMlaVPf < kMlaDvTiles) vread(nt + kMlaVPf);
         const int cb = nt % (kMlaVPf + 1);
         const bf16x8_t a =
             __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vb[cb][0], vb[cb][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int hh = 0; hh < kMlaHT; ++hh)
-          o[hh][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop[hh], o[hh][nt], 0, 0, 0);
+          o[hh][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, pw[hh]), o[hh][nt], 0,
+                                                              0, 0);
+        if (nt & 1) __builtin_amdgcn_sched_barrier(0);
       }
-      stage = stage == kMlaStages - 1 ? 0 : stage + 1;
+    };
+
+    // Before the weights of tile t: mask tokens past the shard's end (last
+    // tile only) and, on a piece's first tile, set the reference max.
+    auto prep = [&](int64_t t) __attribute__((always_inline)) {
+      const int tok0 = static_cast<int>(t - ubeg) * kMlaTile;
+      if (tok0 + kMlaTile > len) {  // uniform
+#pragma unroll
+        for (int hh = 0; hh < kMlaHT; ++hh)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tok0 + 16 * u + 4 * g + i >= len) s_cur[hh][u][i] = -INFINITY;
+      }
+      if (need_ref) {  // uniform
+#pragma unroll
+        for (int hh = 0; hh < kMlaHT; ++hh) {
+          float mt = -INFINITY;
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s_cur[hh][u][i] * c2);
+          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+          m_ref[hh] = mt;
+        }
+        need_ref = false;
+      }
+    };
+
+    scores(lds + stage_of(tile) * kMlaStageBytes, s_cur, no_slice);
+    for (int64_t t = tile; t < piece_end; ++t) {
+      prep(t);
+      if (t + 1 < piece_end) {
+        scores(lds + stage_of(t + 1) * kMlaStageBytes, s_nxt, weight);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2 * kMlaHT * 4; ++j) weight(j);
+        // no score phase here: the pending refill (tile t+3) goes out now,
+        // before end_tile counts on it
+        if (has_pending) {
+#pragma unroll
+          for (int k = 0; k < kMlaDmaPerTile; ++k) dma(pending, k);
+          has_pending = false;
+        }
+      }
+      values(lds + stage_of(t) * kMlaStageBytes, [&]() __attribute__((always_inline)) { begin_tile(t); });
+      end_tile(t);
+#pragma unroll
+      for (int hh = 0; hh < kMlaHT; ++hh) {
+        s_cur[hh][0] = s_nxt[hh][0];
+        s_cur[hh][1] = s_nxt[hh][1];
+      }
     }
+    tile = piece_end;
 
     // ---- replay vote (block-uniform) ------------------------------------------
+    bool bad = false;
+#pragma unroll
+    for (int hh = 0; hh < kMlaHT; ++hh) bad |= mx[hh] > kMlaRefSlack;
     const int wave_bad = __any(bad) ? 1 : 0;  // every lane takes part in the wave vote
     if (lane == 0) *reinterpret_cast<int*>(qrope + wave * kMlaQRopeWaveBytes) = wave_bad;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the vote is in LDS before the barrier
+    wait_lgkm0();  // the vote is in LDS before the barrier
     block_sync();
     int any_bad = 0;
 #pragma unroll
     for (int w = 0; w < kMlaWaves; ++w) any_bad |= *reinterpret_cast<const int*>(qrope + w * kMlaQRopeWaveBytes);
     block_sync();  // every wave has read the votes before they are written again
-    if (any_bad) {
+    // One replay always suffices for finite scores (its reference is the
+    // largest scaled score of the piece); a second vote can only come from
+    // non-finite inputs, which then simply propagate.
+    if (any_bad && !replay) {
+      replay = true;
+      // replay the piece with the largest scaled score seen as the reference
+#pragma unroll
+      for (int hh = 0; hh < kMlaHT; ++hh) {
+        float ms = mx[hh] + m_ref[hh];
+        ms = fmaxf(ms, __shfl_xor(ms, 16, 64));
+        ms = fmaxf(ms, __shfl_xor(ms, 32, 64));
+        m_hint[hh] = ms;
+      }
       wait_vmcnt<0>();
       block_sync();
       tile = piece_tile0;
-      cur_u = piece_u0;
-      pf_t = piece_tile0;
-      pf_u = piece_u0;
-      stage = 0;
-      for (int j = 0; j < kMlaStages - 1 && tile + j < wend; ++j) issue(j);
-#pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = m_seen[hh];
+      cur_u = ld_uniform(ws.wunit + worker);
+      restart(piece_tile0, cur_u);
       continue;
     }
-#pragma unroll
-    for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = -INFINITY;
+    replay = false;
 
     // ---- piece end --------------------------------------------------------------
     const bool whole = (lt_lo == 0) && (lt_hi == uend - ubeg);
