@@ -113,8 +113,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES bytes, 5 times (reference for HBM counters)")
+    ap.add_argument("--calibrate-hbm", type=int, default=0, metavar="BYTES",
+                    help="only run reference kernels for the HBM counters: a plain read (sum) of BYTES bytes "
+                         "and a plain device copy of BYTES bytes, 5 times each")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,13 +134,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda")
+    if args.calibrate_hbm:
+        src = torch.ones(args.calibrate_hbm // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        acc = torch.zeros((), dtype=torch.float32, device="cuda")
         for _ in range(5):
-            dst.copy_(src)
+            acc += src.sum()        # reads BYTES, writes a scalar: reference for FETCH_SIZE
+        for _ in range(5):
+            dst.copy_(src)          # reads and writes BYTES: reference for WRITE_SIZE
         torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "copies": 5}))
+        print(json.dumps({"calibrate_hbm_bytes": args.calibrate_hbm, "reads": 5, "copies": 5,
+                          "check": float(acc) / 5 / src.numel()}))
         return
     w = get_workload(args.workload)
     t_gen = time.perf_counter()
