@@ -57,19 +57,18 @@ constexpr int kMlaRopeOff = kMlaTile * kMlaLatBytes;             // 32768: rope 
 constexpr int kMlaRopeBytes = kMlaRowBytes - kMlaLatBytes;       // 128
 constexpr int kMlaWaves = 4;                                     // wavefronts per workgroup
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32
-constexpr int kMlaHT = kMlaHeadsPerWave / 16;                    // 2 16-head MFMA tiles per wavefront
+constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32: the N side of the MFMAs
 constexpr int kMlaRowsPerWave = kMlaTile / kMlaWaves;            // 8 rows of a tile loaded per wavefront
 constexpr int kMlaDmaPerTile = kMlaRowsPerWave + 1;              // DMA instructions per wavefront and tile
-constexpr int kMlaKSteps = kMlaDk / 32;                          // 18
-constexpr int kMlaKStepsLat = kMlaDv / 32;                       // 16: latent k-steps (Q in VGPRs)
-constexpr int kMlaQRopeWaveBytes = kMlaHT * (kMlaKSteps - kMlaKStepsLat) * 64 * 16;  // 4 KB per wave
-constexpr int kMlaDvTiles = kMlaDv / 16;                         // 32
+constexpr int kMlaKSteps = kMlaDk / 16;                          // 36 score k-steps of 16 dims
+constexpr int kMlaKStepsLat = kMlaDv / 16;                       // 32 latent k-steps (Q in VGPRs)
+constexpr int kMlaQRopeWaveBytes = (kMlaKSteps - kMlaKStepsLat) * 64 * 16;  // 4 KB per wave
+constexpr int kMlaDvTiles = kMlaDv / 32;                         // 16 value M-tiles of 32 dims
 #ifndef DCP_MLA_KPF
 #define DCP_MLA_KPF 3
 #endif
 #ifndef DCP_MLA_VPF
-#define DCP_MLA_VPF 3
+#define DCP_MLA_VPF 4
 #endif
 constexpr int kMlaKPf = DCP_MLA_KPF;  // score-operand read distance (k-steps)
 constexpr int kMlaVPf = DCP_MLA_VPF;  // value-operand read distance (value tiles)
@@ -77,9 +76,10 @@ constexpr int kMlaMaxWorkers = 512;
 constexpr float kMlaRefSlack = 64.f;  // log2 units a score may exceed the piece's reference
 
 static_assert(kMlaStages == 4, "the refill distance below assumes 4 stages");
-static_assert(kMlaKStepsLat == 16 && kMlaKSteps - kMlaKStepsLat == 2, "16 latent + 2 rope k-steps");
+static_assert(kMlaKStepsLat == 32 && kMlaKSteps - kMlaKStepsLat == 4, "32 latent + 4 rope k-steps");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Uniform read-only load through the constant address space (scalar load).
 template <typename T>
@@ -320,27 +320,35 @@ mla_attn_kernel(AttnParams p, int workers) {
   };
 
   // ---- per-lane LDS operand offsets ------------------------------------------
-  // score operand of k-step ks, token half u: row n, chunk 4 ks + g ->
-  //   koff + 2048 ks + 1024 u
-  const int koff = 16 * mla_slot(n, g);
-  // value operand of tile nt (dims 16 nt .. +15), token half u: the lane
-  // addresses row 4 g + n / 4, dims 16 nt + 4 (n % 4) .. +3, i.e. chunk
-  // 4 (nt / 2) + c with c = 2 (nt % 2) + (n % 4) / 2, byte 8 ((n % 4) % 2) ->
-  //   voff[nt % 2] + 2048 (nt / 2) + 1024 u
+  // Lane l = 32 h + c32 (h = l / 32), and in 16-lane groups l = 16 G + 4 i + j.
+  // Score operand (A of v_mfma_f32_32x32x16_bf16) of k-step ks (dims 16 ks
+  // .. +15): token row c32, dims 16 ks + 8 h .. +7, i.e. 32-dim block ks / 2,
+  // token half c32 / 16, chunk 2 (ks % 2) + h of row c32 % 16:
+  //   koff[ks % 2] + 2048 (ks / 2)
+  int koff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) koff[q] = ((lane >> 4) & 1) * 1024 + 16 * mla_slot(lane & 15, 2 * q + (lane >> 5));
+  // Value operand (A) of M-tile mt (dims 32 mt .. +31) and token step kk
+  // (tokens 16 kk .. +15), through two transpose reads rd = 0, 1: the lane
+  // addresses token 8 (G / 2) + 4 rd + i of half kk and dims 32 mt + 16 (G % 2)
+  // + 4 j .. +3, i.e. chunk 2 (G % 2) + j / 2, byte 8 (j % 2):
+  //   voff[rd] + 2048 mt + 1024 kk
+  // and receives dim 32 mt + l % 32, tokens 8 h + 4 rd .. +3 of the step.
   int voff[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    voff[q] = 16 * mla_slot(4 * g + (n >> 2), 2 * q + ((n & 3) >> 1)) + 8 * (n & 1);
+  for (int rd = 0; rd < 2; ++rd) {
+    const int G = lane >> 4, i = (lane & 15) >> 2, j = lane & 3;
+    voff[rd] = 16 * mla_slot(8 * (G >> 1) + 4 * rd + i, 2 * (G & 1) + (j >> 1)) + 8 * (j & 1);
+  }
   char* qr = qrope + wave * kMlaQRopeWaveBytes + lane * 16;
 
   restart(wstart, ld_uniform(ws.wunit + worker));
 
   int64_t cur_u = ld_uniform(ws.wunit + worker);  // unit of the tile being computed
   int64_t tile = wstart;
-  float m_hint[kMlaHT];  // reference for a replayed piece
-  bool replay = false;   // the current piece is a replay (at most one per piece)
-#pragma unroll
-  for (int hh = 0; hh < kMlaHT; ++hh) m_hint[hh] = -INFINITY;
+  float m_hint = -INFINITY;  // reference for a replayed piece (this lane's head)
+  bool replay = false;       // the current piece is a replay (at most one per piece)
+  const int h = lane >> 5;   // token quarter-row group of the score layout, k-half of the operands
 
   while (tile < wend) {
     while (ld_uniform(ws.prefix + cur_u + 1) <= tile) ++cur_u;
@@ -351,22 +359,19 @@ mla_attn_kernel(AttnParams p, int workers) {
                                static_cast<int>(cur_u / p.batch));
     const int64_t piece_tile0 = tile, piece_end = tile + (lt_hi - lt_lo);
 
-    // Q operand (B of the score MFMA): head 32 wave + 16 hh + n, dims 32 ks +
-    // 8 g .. +8; latent k-steps in VGPRs, rope k-steps in this wave's slice
-    bf16x8_t qop[kMlaHT][kMlaKStepsLat];
+    // Q operand (B of the score MFMA): head 32 wave + l % 32, dims 16 ks + 8 h
+    // .. +7; latent k-steps in VGPRs, rope k-steps in this wave's LDS slice
+    bf16x8_t qop[kMlaKStepsLat];
     {
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) +
-                           (static_cast<int64_t>(b) * kMlaHeads + kMlaHeadsPerWave * wave + n) * kMlaDk + 8 * g;
+                           (static_cast<int64_t>(b) * kMlaHeads + kMlaHeadsPerWave * wave + (lane & 31)) * kMlaDk +
+                           8 * h;
 #pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) {
+      for (int ks = 0; ks < kMlaKStepsLat; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * ks);
 #pragma unroll
-        for (int ks = 0; ks < kMlaKStepsLat; ++ks)
-          qop[hh][ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
-#pragma unroll
-        for (int ks = kMlaKStepsLat; ks < kMlaKSteps; ++ks)
-          *reinterpret_cast<bf16x8_t*>(qr + (hh * (kMlaKSteps - kMlaKStepsLat) + ks - kMlaKStepsLat) * 1024) =
-              *reinterpret_cast<const bf16x8_t*>(qb + 16 * hh * kMlaDk + 32 * ks);
-      }
+      for (int ks = kMlaKStepsLat; ks < kMlaKSteps; ++ks)
+        *reinterpret_cast<bf16x8_t*>(qr + (ks - kMlaKStepsLat) * 1024) =
+            *reinterpret_cast<const bf16x8_t*>(qb + 16 * ks);
     }
     // Q is complete here, so no wait for it lands inside the tile loop (where
     // it would also drain the tiles in flight).
@@ -376,70 +381,56 @@ mla_attn_kernel(AttnParams p, int workers) {
     // ---- piece state ------------------------------------------------------------
     // Weights are exp2(s c2 - m_ref) with m_ref fixed for the piece (the first
     // tile's max unless a replay hands one in); mx tracks the largest exponent
-    // seen, for the replay vote and the next reference.
-    float m_ref[kMlaHT], mx[kMlaHT], l[kMlaHT], e[kMlaHT];
-    f32x4_t o[kMlaHT][kMlaDvTiles];
+    // seen, for the replay vote and the next reference. O^T[dim, head] of M-tile
+    // mt: lane l holds head l % 32, dims 32 mt + 8 (r / 4) + 4 h + r % 4.
+    float m_ref = m_hint, mx = -INFINITY, lsum = 0.f, esum = 0.f;
+    f32x16_t o[kMlaDvTiles];
 #pragma unroll
-    for (int hh = 0; hh < kMlaHT; ++hh) {
-      m_ref[hh] = m_hint[hh];
-      mx[hh] = -INFINITY;
-      l[hh] = 0.f;
-      e[hh] = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < kMlaDvTiles; ++nt) o[hh][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mt = 0; mt < kMlaDvTiles; ++mt) o[mt] = f32x16_t{};
     bool need_ref = !replay;  // uniform
 
-    // ---- score MFMAs of one tile, with `slice(ks)` (VALU work of the previous
-    // tile) placed after the MFMAs of k-step ks -----------------------------------
-    auto scores = [&](const char* st, f32x4_t (&s)[kMlaHT][2], auto&& slice) __attribute__((always_inline)) {
-#pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) s[hh][0] = s[hh][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* kb = st + koff;
-      bf16x8_t ka[kMlaKPf + 1][2];
+    // ---- score MFMAs of one tile: S^T[token, head], lane l holding head l % 32,
+    // tokens 8 (r / 4) + 4 h + r % 4 of register r; `slice(ks)` (VALU work of
+    // the previous tile) goes after k-step ks's MFMA, which depends on the one
+    // before it ------------------------------------------------------------------
+    auto scores = [&](const char* st, f32x16_t& s, auto&& slice) __attribute__((always_inline)) {
+      s = f32x16_t{};
+      bf16x8_t ka[kMlaKPf + 1];
+      bf16x8_t qx[kMlaKSteps - kMlaKStepsLat];  // rope Q, read from LDS with the rope K rows
       auto kread = [&](int ks) __attribute__((always_inline)) {
-        ka[ks % (kMlaKPf + 1)][0] = *reinterpret_cast<const bf16x8_t*>(kb + 2048 * ks);
-        ka[ks % (kMlaKPf + 1)][1] = *reinterpret_cast<const bf16x8_t*>(kb + 2048 * ks + 1024);
+        ka[ks % (kMlaKPf + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff[ks & 1] + 2048 * (ks >> 1));
+        if (ks >= kMlaKStepsLat)
+          qx[ks - kMlaKStepsLat] = *reinterpret_cast<const bf16x8_t*>(qr + (ks - kMlaKStepsLat) * 1024);
       };
 #pragma unroll
       for (int j = 0; j < kMlaKPf; ++j) kread(j);
 #pragma unroll
       for (int ks = 0; ks < kMlaKSteps; ++ks) {
         if (ks + kMlaKPf < kMlaKSteps) kread(ks + kMlaKPf);
-#pragma unroll
-        for (int hh = 0; hh < kMlaHT; ++hh) {
-          bf16x8_t bq;
-          if (ks < kMlaKStepsLat)
-            bq = qop[hh][ks < kMlaKStepsLat ? ks : 0];
-          else
-            bq = *reinterpret_cast<const bf16x8_t*>(
-                qr + (hh * (kMlaKSteps - kMlaKStepsLat) + ks - kMlaKStepsLat) * 1024);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            s[hh][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % (kMlaKPf + 1)][u], bq, s[hh][u], 0, 0, 0);
-        }
+        const bf16x8_t bq = ks < kMlaKStepsLat ? qop[ks < kMlaKStepsLat ? ks : 0]
+                                               : qx[ks < kMlaKStepsLat ? 0 : ks - kMlaKStepsLat];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kMlaKPf + 1)], bq, s, 0, 0, 0);
         slice(ks);
         pending_dma(ks);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // ---- softmax of one tile: weight j of this lane (head tile j / 8, token
-    // 16 ((j / 4) % 2) + 4 g + j % 4), one per slice --------------------------------
-    f32x4_t s_cur[kMlaHT][2], s_nxt[kMlaHT][2];
-    u32x4_t pw[kMlaHT];  // packed bf16 weights: the B operand of the value MFMA
+    // ---- softmax of one tile: weight r (0 .. 15) of this lane, one per slice;
+    // pw[d] packs weights 2 d, 2 d + 1 (tokens 8 (d / 2) + 4 h + 2 (d % 2) + {0, 1})
+    f32x16_t s_cur, s_nxt;
+    uint32_t pw[8];
     float pe_lo = 0.f;
-    auto weight = [&](int j) __attribute__((always_inline)) {
-      if (j >= 2 * kMlaHT * 4) return;
-      const int hh = j >> 3, u = (j >> 2) & 1, i = j & 3;
-      const float x = fmaf(s_cur[hh][u][i], c2, -m_ref[hh]);
-      mx[hh] = fmaxf(mx[hh], x);
+    auto weight = [&](int r) __attribute__((always_inline)) {
+      if (r >= 16) return;
+      const float x = fmaf(s_cur[r], c2, -m_ref);
+      mx = fmaxf(mx, x);
       const float pe = __builtin_amdgcn_exp2f(x);  // v_exp_f32; results below 2^-126 flush to 0
-      e[hh] += pe;
-      if (i & 1) {
+      esum += pe;
+      if (r & 1) {
         const bf16x2_t pk = pack_bf16(pe_lo, pe);
-        pw[hh][2 * u + (i >> 1)] = __builtin_bit_cast(uint32_t, pk);
-        l[hh] = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{__bf16(1.f), __bf16(1.f)}, l[hh], false);
+        pw[r >> 1] = __builtin_bit_cast(uint32_t, pk);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{__bf16(1.f), __bf16(1.f)}, lsum, false);
       } else {
         pe_lo = pe;
       }
@@ -447,29 +438,42 @@ mla_attn_kernel(AttnParams p, int workers) {
     auto no_slice = [](int) __attribute__((always_inline)) {};
 
     // ---- value MFMAs of one tile --------------------------------------------------
+    // B operand of token step kk: lane l needs head l % 32, tokens 16 kk + 8 h ..
+    // +7. A lane holds tokens 4 h + {0..3} + 8 q (q = 2 kk, 2 kk + 1): swapping the
+    // upper half of the q = 2 kk words with the lower half of the q = 2 kk + 1
+    // words (v_permlane32_swap) gives every lane its 8 tokens, in order.
     auto values = [&](const char* st, auto&& side) __attribute__((always_inline)) {
-      const char* vbase0 = st + voff[0];
-      const char* vbase1 = st + voff[1];
+      u32x4_t pb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(pw[4 * kk + w2], pw[4 * kk + 2 + w2], false, false);
+          pb[kk][w2] = sw[0];
+          pb[kk][2 + w2] = sw[1];
+        }
+      }
+      // step idx = 16 kk + mt (kk outer, so that the two MFMAs into one
+      // accumulator are 16 apart): two transpose reads, kept in a ring indexed
+      // by the step
       s16x4_t vb[kMlaVPf + 1][2];
-      auto vread = [&](int nt) __attribute__((always_inline)) {
-        const char* a1 = ((nt & 1) ? vbase1 : vbase0) + 2048 * (nt >> 1);
-        vb[nt % (kMlaVPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1));
-        vb[nt % (kMlaVPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a1 + 1024));
+      auto vread = [&](int idx) __attribute__((always_inline)) {
+        const int mt = idx & 15, kk = idx >> 4;
+        const char* a0 = st + 2048 * mt + 1024 * kk;
+        vb[idx % (kMlaVPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0 + voff[0]));
+        vb[idx % (kMlaVPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0 + voff[1]));
       };
 #pragma unroll
       for (int j = 0; j < kMlaVPf; ++j) vread(j);
 #pragma unroll
-      for (int nt = 0; nt < kMlaDvTiles; ++nt) {
-        if (nt == 2) side();  // scalar work in the shadow of the MFMAs
-        if (nt + kMlaVPf < kMlaDvTiles) vread(nt + kMlaVPf);
-        const int cb = nt % (kMlaVPf + 1);
-        const bf16x8_t a =
-            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vb[cb][0], vb[cb][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int hh = 0; hh < kMlaHT; ++hh)
-          o[hh][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, pw[hh]), o[hh][nt], 0,
-                                                              0, 0);
-        if (nt & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int idx = 0; idx < 2 * kMlaDvTiles; ++idx) {
+        if (idx == 2) side();  // scalar work in the shadow of the MFMAs
+        if (idx + kMlaVPf < 2 * kMlaDvTiles) vread(idx + kMlaVPf);
+        const int mt = idx & 15, kk = idx >> 4;
+        const s16x4_t* v = vb[idx % (kMlaVPf + 1)];
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pb[kk]), o[mt], 0, 0, 0);
+        if (idx & 1) __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -479,25 +483,14 @@ mla_attn_kernel(AttnParams p, int workers) {
       const int tok0 = static_cast<int>(t - ubeg) * kMlaTile;
       if (tok0 + kMlaTile > len) {  // uniform
 #pragma unroll
-        for (int hh = 0; hh < kMlaHT; ++hh)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (tok0 + 16 * u + 4 * g + i >= len) s_cur[hh][u][i] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if (tok0 + 8 * (r >> 2) + 4 * h + (r & 3) >= len) s_cur[r] = -INFINITY;
       }
       if (need_ref) {  // uniform
+        float mt = -INFINITY;
 #pragma unroll
-        for (int hh = 0; hh < kMlaHT; ++hh) {
-          float mt = -INFINITY;
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s_cur[hh][u][i] * c2);
-          mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-          m_ref[hh] = mt;
-        }
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_cur[r] * c2);
+        m_ref = fmaxf(mt, __shfl_xor(mt, 32, 64));
         need_ref = false;
       }
     };
@@ -509,7 +502,7 @@ mla_attn_kernel(AttnParams p, int workers) {
         scores(lds + stage_of(t + 1) * kMlaStageBytes, s_nxt, weight);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2 * kMlaHT * 4; ++j) weight(j);
+        for (int r = 0; r < 16; ++r) weight(r);
         // no score phase here: the pending refill (tile t+3) goes out now,
         // before end_tile counts on it
         if (has_pending) {
@@ -520,19 +513,12 @@ mla_attn_kernel(AttnParams p, int workers) {
       }
       values(lds + stage_of(t) * kMlaStageBytes, [&]() __attribute__((always_inline)) { begin_tile(t); });
       end_tile(t);
-#pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) {
-        s_cur[hh][0] = s_nxt[hh][0];
-        s_cur[hh][1] = s_nxt[hh][1];
-      }
+      s_cur = s_nxt;
     }
     tile = piece_end;
 
     // ---- replay vote (block-uniform) ------------------------------------------
-    bool bad = false;
-#pragma unroll
-    for (int hh = 0; hh < kMlaHT; ++hh) bad |= mx[hh] > kMlaRefSlack;
-    const int wave_bad = __any(bad) ? 1 : 0;  // every lane takes part in the wave vote
+    const int wave_bad = __any(mx > kMlaRefSlack) ? 1 : 0;  // every lane takes part in the wave vote
     if (lane == 0) *reinterpret_cast<int*>(qrope + wave * kMlaQRopeWaveBytes) = wave_bad;
     wait_lgkm0();  // the vote is in LDS before the barrier
     block_sync();
@@ -546,13 +532,8 @@ mla_attn_kernel(AttnParams p, int workers) {
     if (any_bad && !replay) {
       replay = true;
       // replay the piece with the largest scaled score seen as the reference
-#pragma unroll
-      for (int hh = 0; hh < kMlaHT; ++hh) {
-        float ms = mx[hh] + m_ref[hh];
-        ms = fmaxf(ms, __shfl_xor(ms, 16, 64));
-        ms = fmaxf(ms, __shfl_xor(ms, 32, 64));
-        m_hint[hh] = ms;
-      }
+      const float ms = mx + m_ref;
+      m_hint = fmaxf(ms, __shfl_xor(ms, 32, 64));
       wait_vmcnt<0>();
       block_sync();
       tile = piece_tile0;
@@ -561,34 +542,37 @@ mla_attn_kernel(AttnParams p, int workers) {
       continue;
     }
     replay = false;
+    m_hint = -INFINITY;
 
     // ---- piece end --------------------------------------------------------------
     const bool whole = (lt_lo == 0) && (lt_hi == uend - ubeg);
     const int which = (lt_lo == 0) ? 1 : 0;  // 0: the unit began before this worker
+    const float lt_ = lsum + __shfl_xor(lsum, 32, 64);
+    const float et = esum + __shfl_xor(esum, 32, 64);
+    const int head = kMlaHeadsPerWave * wave + (lane & 31);
+    if (whole) {
+      const int64_t row = cur_u * kMlaHeads + head;
+      float* dst = p.out_o + row * kMlaDv + 4 * h;
+      const float inv = 1.f / lt_;
 #pragma unroll
-    for (int hh = 0; hh < kMlaHT; ++hh) {
-      float lt_ = l[hh] + __shfl_xor(l[hh], 16, 64);
-      lt_ += __shfl_xor(lt_, 32, 64);
-      float et = e[hh] + __shfl_xor(e[hh], 16, 64);
-      et += __shfl_xor(et, 32, 64);
-      const int head = kMlaHeadsPerWave * wave + 16 * hh + n;
-      if (whole) {
-        const int64_t row = cur_u * kMlaHeads + head;
-        float* dst = p.out_o + row * kMlaDv + 4 * g;
-        const float inv = 1.f / lt_;
+      for (int mt = 0; mt < kMlaDvTiles; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < kMlaDvTiles; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt) = o[hh][nt] * inv;
-        if (g == 0) p.out_lse[row] = (m_ref[hh] + __log2f(et)) * DCP_LN2;
-      } else {
-        float* dst =
-            ws.part + ((static_cast<int64_t>(worker) * 2 + which) * kMlaHeads + head) * (kMlaDv + kPartExtra);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + 32 * mt + 8 * q) =
+              f32x4_t{o[mt][4 * q], o[mt][4 * q + 1], o[mt][4 * q + 2], o[mt][4 * q + 3]} * inv;
+      if (h == 0) p.out_lse[row] = (m_ref + __log2f(et)) * DCP_LN2;
+    } else {
+      float* dst = ws.part + ((static_cast<int64_t>(worker) * 2 + which) * kMlaHeads + head) * (kMlaDv + kPartExtra);
 #pragma unroll
-        for (int nt = 0; nt < kMlaDvTiles; ++nt) *reinterpret_cast<f32x4_t*>(dst + 16 * nt + 4 * g) = o[hh][nt];
-        if (g == 0) {
-          dst[kMlaDv] = m_ref[hh];
-          dst[kMlaDv + 1] = lt_;
-          dst[kMlaDv + 2] = et;
-        }
+      for (int mt = 0; mt < kMlaDvTiles; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + 32 * mt + 8 * q + 4 * h) =
+              f32x4_t{o[mt][4 * q], o[mt][4 * q + 1], o[mt][4 * q + 2], o[mt][4 * q + 3]};
+      if (h == 0) {
+        dst[kMlaDv] = m_ref;
+        dst[kMlaDv + 1] = lt_;
+        dst[kMlaDv + 2] = et;
       }
     }
   }
