@@ -65,10 +65,10 @@ constexpr int kMlaKStepsLat = kMlaDv / 16;                       // 32 latent k-
 constexpr int kMlaQRopeWaveBytes = (kMlaKSteps - kMlaKStepsLat) * 64 * 16;  // 4 KB per wave
 constexpr int kMlaDvTiles = kMlaDv / 32;                         // 16 value M-tiles of 32 dims
 #ifndef DCP_MLA_KPF
-#define DCP_MLA_KPF 3
+#define DCP_MLA_KPF 4
 #endif
 #ifndef DCP_MLA_VPF
-#define DCP_MLA_VPF 4
+#define DCP_MLA_VPF 6
 #endif
 constexpr int kMlaKPf = DCP_MLA_KPF;  // score-operand read distance (k-steps)
 constexpr int kMlaVPf = DCP_MLA_VPF;  // value-operand read distance (value tiles)
@@ -190,6 +190,7 @@ mla_attn_kernel(AttnParams p, int workers) {
     int64_t t, u, ubeg, uend;
     bool fresh;
     int len, vb, off;
+    int vb_loaded, blk;  // the last block-table entry read (consecutive tiles often share it)
     const int32_t* bt;
     const char* rk;
   };
@@ -206,6 +207,8 @@ mla_attn_kernel(AttnParams p, int workers) {
     w.uend = ld_uniform(ws.prefix + u + 1);
     w.fresh = true;
     w.len = w.vb = w.off = 0;
+    w.vb_loaded = -1;
+    w.blk = 0;
     w.bt = p.block_table;
     w.rk = kbase;
     return w;
@@ -225,19 +228,29 @@ mla_attn_kernel(AttnParams p, int workers) {
       const int t0 = static_cast<int>(w.t - w.ubeg) * kMlaTile;
       w.vb = t0 / bs;
       w.off = t0 - w.vb * bs;
+      w.vb_loaded = -1;
       w.fresh = false;
+    }
+    if (w.vb != w.vb_loaded) {  // uniform
+      w.blk = ld_uniform(w.bt + w.vb);
+      w.vb_loaded = w.vb;
     }
     const int t0 = static_cast<int>(w.t - w.ubeg) * kMlaTile;
     TileSrc src;
     src.nv0 = min(16, w.len - t0);
     const int nv1 = min(16, w.len - t0 - 16);
-    src.base0 = w.rk + (static_cast<int64_t>(ld_uniform(w.bt + w.vb)) * ks1 + w.off * ks3) * 2;
+    src.base0 = w.rk + (static_cast<int64_t>(w.blk) * ks1 + w.off * ks3) * 2;
     src.base1 = src.base0;
     src.nv1 = src.nv0;
     if (nv1 > 0) {  // uniform
       int off_b = w.off + 16, vb_b = w.vb;
-      if (off_b >= bs) { off_b -= bs; ++vb_b; }
-      src.base1 = w.rk + (static_cast<int64_t>(ld_uniform(w.bt + vb_b)) * ks1 + off_b * ks3) * 2;
+      int blk_b = w.blk;
+      if (off_b >= bs) {  // uniform: the second half starts a new block
+        off_b -= bs;
+        ++vb_b;
+        blk_b = ld_uniform(w.bt + vb_b);
+      }
+      src.base1 = w.rk + (static_cast<int64_t>(blk_b) * ks1 + off_b * ks3) * 2;
       src.nv1 = nv1;
     }
     ++w.t;
@@ -274,49 +287,46 @@ mla_attn_kernel(AttnParams p, int workers) {
   auto dma = [&](const Refill& r, int k) __attribute__((always_inline)) {
     dma16_s(r.voff + 128 * k, r.base, r.m0 + 4096 * k);
   };
-  Refill next_refill;          // prepared refill (valid when has_next)
-  bool has_next = false;       // uniform
-  Refill pending;              // refill whose DMAs the next score phase issues
-  bool has_pending = false;    // uniform
+  // Every tile step issues exactly one refill (9 DMAs per wave): once the
+  // worker's tiles run out, the last real refill is issued again (it rewrites
+  // a stage with the data it already holds), so every wait count below is a
+  // constant and no branch guards a DMA. The kernel drains them before exit.
+  Refill next_refill;  // the refill prepared during the current tile
+  Refill pending;      // the refill the next score phase issues
 
   // (Re)start the ring at tile t (unit u): load tiles t .. t+3 at once and
   // wait until the first two have landed everywhere.
   auto restart = [&](int64_t t, int64_t u) __attribute__((always_inline)) {
     dw = walker_at(t, u);
-    has_next = has_pending = false;
-    for (int j = 0; j < kMlaStages && t + j < wend; ++j) {
-      const Refill r = prepare();
+    for (int j = 0; j < kMlaStages; ++j) {
+      if (t + j < wend) next_refill = prepare();  // uniform
 #pragma unroll
-      for (int k = 0; k < kMlaDmaPerTile; ++k) dma(r, k);
+      for (int k = 0; k < kMlaDmaPerTile; ++k) dma(next_refill, k);
     }
-    const int64_t later = min<int64_t>(max<int64_t>(wend - t - 2, 0), 2);  // tiles allowed in flight
-    if (later == 2) wait_vmcnt<2 * kMlaDmaPerTile>();
-    else if (later == 1) wait_vmcnt<kMlaDmaPerTile>();
-    else wait_vmcnt<0>();
+    // the next score phase re-issues the last refill: same data into the same
+    // stage (a duplicate step only makes the next waits more conservative)
+    pending = next_refill;
+    wait_vmcnt<2 * kMlaDmaPerTile>();
     block_sync();
   };
   // During tile t's value phase: prepare the refill with tile t+4 (issued
   // after the barrier that ends tile t).
   auto begin_tile = [&](int64_t t) __attribute__((always_inline)) {
-    has_next = t + kMlaStages < wend;
-    if (has_next) next_refill = prepare();
+    if (t + kMlaStages < wend) next_refill = prepare();  // uniform
   };
   // End of tile t (every read of its stage issued): wait until tile t+2 has
-  // landed; the refill of t's stage with tile t+4 becomes pending. Tile t+3's
-  // DMAs were issued during this iteration's score phase (or by restart), so
-  // they are the only ones allowed to stay in flight.
-  auto end_tile = [&](int64_t t) __attribute__((always_inline)) {
+  // landed; the refill of t's stage with tile t+4 becomes pending. The step
+  // after t+2's (issued during this iteration's score phase, or by restart)
+  // is the only one allowed to stay in flight.
+  auto end_tile = [&](int64_t) __attribute__((always_inline)) {
     wait_lgkm0();
-    if (t + 3 < wend) wait_vmcnt<kMlaDmaPerTile>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<kMlaDmaPerTile>();
     block_sync();
     pending = next_refill;
-    has_pending = has_next;
   };
-  // DMA j of the pending refill, issued after k-step 2 j of a score phase
+  // DMA j of the pending refill, issued after k-step 4 j of a score phase
   auto pending_dma = [&](int ks) __attribute__((always_inline)) {
-    if ((ks & 1) == 0 && ks / 2 < kMlaDmaPerTile && has_pending) dma(pending, ks / 2);
-    if (ks == 2 * (kMlaDmaPerTile - 1)) has_pending = false;
+    if ((ks & 3) == 0 && ks / 4 < kMlaDmaPerTile) dma(pending, ks / 4);
   };
 
   // ---- per-lane LDS operand offsets ------------------------------------------
@@ -503,13 +513,10 @@ mla_attn_kernel(AttnParams p, int workers) {
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) weight(r);
-        // no score phase here: the pending refill (tile t+3) goes out now,
-        // before end_tile counts on it
-        if (has_pending) {
+        // no score phase here: the pending refill goes out now, before
+        // end_tile counts on it
 #pragma unroll
-          for (int k = 0; k < kMlaDmaPerTile; ++k) dma(pending, k);
-          has_pending = false;
-        }
+        for (int k = 0; k < kMlaDmaPerTile; ++k) dma(pending, k);
       }
       values(lds + stage_of(t) * kMlaStageBytes, [&]() __attribute__((always_inline)) { begin_tile(t); });
       end_tile(t);
@@ -576,6 +583,7 @@ mla_attn_kernel(AttnParams p, int workers) {
       }
     }
   }
+  wait_vmcnt<0>();  // refills issued past the last tile still write this workgroup's LDS
 }
 
 // ---------------------------------------------------------------------------
