@@ -15,6 +15,12 @@ What it computes, each function citing the passage it follows:
                   section "KV-cache layout", evaluated literally, plus a running
                   per-rank counter; local sequence lengths are the counters'
                   final values.
+* ``cache``     - the KV-cache write: new rows stored (fp32 as is, bf16 and fp8
+                  e4m3 by nearest-value rounding, fp8 through the per-head
+                  scale) at the slots the slot mapping gives, non-owners
+                  skipped ("Decode Context Parallel (DCP)", section "DCP slot
+                  mapping"; "DeepSeek V4.1 context parallelism", section
+                  "Cache ownership").
 * ``attention`` - plain full-softmax decode attention over the *unsharded*
                   sequence in float64, the per-rank partial (O, LSE) over the
                   tokens a rank owns, and the log-sum-exp merge with an
@@ -23,8 +29,9 @@ What it computes, each function citing the passage it follows:
 
 Every function here is pinned by ``-m "not gpu"`` tests against something other
 than itself (hand-derived worked example, closed forms, invariants, torch's
-float64 scaled-dot-product attention, torch's float8 decoding, brute force).
+float64 scaled-dot-product attention, torch's float8 decoding, brute force,
+the E4M3 code table's own values).
 No function is "parity unpinned".
 """
 
-from . import formats, layout, attention  # noqa: F401
+from . import formats, layout, attention, cache  # noqa: F401

@@ -46,7 +46,8 @@ _E4M3_TABLE = e4m3fn_table()
 def decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> float64 (exact: bf16 widens into binary32)."""
     b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns decode to NaN
+        return b.view(np.float32).astype(np.float64)
 
 
 def decode(stored: np.ndarray, fmt: str) -> np.ndarray:
