@@ -17,6 +17,11 @@ distributions of the named workload). Prints ONE JSON line:
 * ``cpu_baseline`` - the float64 CPU oracle timed on a bounded sample of the
                 same batch (rank 0, N = 1 only).
 
+With ``--workload kvw_*`` a step is instead the KV-cache write of a batch of
+new tokens (slot mapping, then the write of every row into its owner's pool);
+``value`` and ``roofline`` then count the write's algorithmic bytes (new rows
+read, one slot per rank read, stored rows written once).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
@@ -33,8 +38,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU"
 DEFAULT_WORKLOAD = "gqa_fp8_binned"
-KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel"}
-KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip"}
+KV_WRITE_METRIC = "KV-cache write GB/s (new rows + slots read, stored rows written) at 1 GPU"
+KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
+                "kv_write": "kv_write_kernel"}
+KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip",
+                  "kv_write": "kv_write.hip"}
 
 
 def kernel_family(w):
@@ -105,6 +113,147 @@ def cpu_baseline(case, budget_s):
     }
 
 
+def cpu_baseline_kv_write(case, budget_s):
+    """Time the oracle's slot mapping + cache write on request-sized pieces of
+    the batch (~budget_s)."""
+    import numpy as np
+    from oracle import cache as ocache
+    from oracle import formats as ofmt
+    from oracle import layout as olay
+    from workloads.generate import stored_numpy
+    w, g = case.workload, case.workload.geometry()
+    R, H, bs = g.dcp_size, g.num_kv_heads, g.block_size
+    fmt = g.kv_format
+    np_t = {"fp32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}[fmt]
+    k_all, v_all = stored_numpy(case.k_new), None if case.v_new is None else stored_numpy(case.v_new)
+    spent, tokens, reqs = 0.0, 0, 0
+    for b in range(w.requests):
+        lo, hi = b * w.chunk, (b + 1) * w.chunk
+        # a pool of just this request's blocks keeps the sample's memory bounded
+        used = case.block_table[b][case.block_table[b] >= 0]
+        table = np.full_like(case.block_table[b:b + 1], -1)
+        table[0, :used.size] = np.arange(used.size, dtype=np.int32)
+        kp = np.zeros((R, max(used.size, 1), H, bs, g.head_dim_k), dtype=np_t)
+        vp = None if g.mla else np.zeros((R, max(used.size, 1), H, g.head_dim_v, bs), dtype=np_t)
+        t0 = time.perf_counter()
+        k = k_all[lo:hi] if w.src_format == "fp32" else ofmt.decode(k_all[lo:hi], ofmt.BF16).astype(np.float32)
+        v = None
+        if v_all is not None:
+            v = v_all[lo:hi] if w.src_format == "fp32" else ofmt.decode(v_all[lo:hi], ofmt.BF16).astype(np.float32)
+        slots = olay.slot_mapping(case.positions[lo:hi], np.zeros(hi - lo, dtype=np.int32), table, bs, R,
+                                  g.interleave)
+        ocache.cache_write(kp, vp, k, v, slots, bs, fmt, case.k_scale, case.v_scale)
+        spent += time.perf_counter() - t0
+        tokens += hi - lo
+        reqs += 1
+        if spent >= budget_s:
+            break
+    return {
+        "value": tokens * w.bytes_per_token() / spent / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{reqs} of {w.requests} requests ({tokens} of {w.tokens} tokens), slot mapping + "
+                   f"quantise + placement in numpy, each request into a pool of its own blocks; {spent:.1f} s"),
+    }
+
+
+def bench_kv_write(args, name):
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from workloads import get_kv_write_workload, make_kv_write_case
+    from workloads.generate import TORCH_FORMAT
+
+    w = get_kv_write_workload(name)
+    g = w.geometry()
+    dev = "cuda"
+    t_gen = time.perf_counter()
+    case = make_kv_write_case(w, dev)
+    R, N, H, bs = g.dcp_size, case.num_blocks, g.num_kv_heads, g.block_size
+    pool = dcp.PagedKVCache(R, N, bs, H, g.head_dim_k, g.head_dim_v, TORCH_FORMAT[g.kv_format], mla=g.mla,
+                            device=dev, k_scale=case.k_scale, v_scale=case.v_scale)
+    desc = pool.descriptor()
+    positions = torch.from_numpy(case.positions).to(dev)
+    reqs = torch.from_numpy(case.req_indices).to(dev)
+    table = torch.from_numpy(case.block_table).to(dev)
+    slots = torch.empty((R, w.tokens), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name}: {w.tokens} tokens into {R} ranks x {N} blocks, "
+          f"{w.tokens * w.bytes_per_token() / 1e6:.1f} MB per write, inputs ready in {t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    def step():
+        dcp.dcp_slot_mapping(positions, reqs, table, bs, R, g.interleave, out=slots)
+        dcp.dcp_kv_cache_write(case.k_new, case.v_new, slots, desc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # the write kernel alone, on the stream it is launched on (torch's current stream)
+    start.record()
+    for _ in range(args.steps):
+        dcp.dcp_kv_cache_write(case.k_new, case.v_new, slots, desc)
+    stop.record()
+    torch.cuda.synchronize()
+    kern_ms = start.elapsed_time(stop) / args.steps
+
+    nbytes = w.tokens * w.bytes_per_token()
+    out = {
+        "metric": KV_WRITE_METRIC,
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[g.kv_format],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "tokens": w.tokens,
+            "requests": w.requests,
+            "chunk": w.chunk,
+            "num_kv_heads": H,
+            "head_dim_k": g.head_dim_k,
+            "head_dim_v": g.head_dim_v,
+            "kv_format": g.kv_format,
+            "src_format": w.src_format,
+            "mla": g.mla,
+            "block_size": bs,
+            "dcp_size": R,
+            "interleave": g.interleave,
+            "bytes_per_token": w.bytes_per_token(),
+            "tokens_per_s": round(w.tokens / (ms * 1e-3), 1),
+            "kernel": KERNEL_NAMES["kv_write"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic("kv_write", w.name),
+            "kernel_avg_ms": round(kern_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_kv_write(case, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +294,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_hbm_bytes": args.calibrate_hbm, "reads": 5, "copies": 5,
                           "check": float(acc) / 5 / src.numel()}))
+        return
+    if args.workload.startswith("kvw_"):
+        bench_kv_write(args, args.workload)
         return
     w = get_workload(args.workload)
     t_gen = time.perf_counter()

@@ -235,6 +235,50 @@ int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts,
                   void* out_o, float* out_lse, void* stream);
 
 /*
+ * dcp_kv_cache_write - store new tokens' K and V rows into the pools of the
+ * ranks that own them.
+ *
+ * Source: "Decode Context Parallel (DCP)", section "KV-cache layout" (each
+ * rank stores only the tokens of its shard, at the slot given by the slot
+ * mapping); "DeepSeek V4.1 context parallelism", section "Cache ownership"
+ * (a cache write turns the virtual slot into the owner's local slot; ranks
+ * that do not own the token write nothing).
+ *
+ * For token t and rank r in [0, num_ranks), with s = slots[r * num_tokens + t]:
+ * if 0 <= s < num_blocks * block_size, then for every kv head h and dim d
+ *   K[r, s / block_size, h, s % block_size, d] = store(k_new[t, h, d], k_scale[h])
+ *   V[r, s / block_size, h, s % block_size, d] = store(v_new[t, h, d], v_scale[h])
+ * (addresses as in dcp_kv_cache_t); any other s (-1 for a rank that does not
+ * own the token) writes nothing on rank r. store() by kv->dtype:
+ *   DCP_F32       the fp32 value of the input;
+ *   DCP_BF16      the input rounded to the nearest bf16, ties to even
+ *                 (NaN stays a quiet NaN);
+ *   DCP_FP8_E4M3  the E4M3 code nearest to the fp32 quotient x / scale[h]
+ *                 (IEEE division), ties to the even code; magnitudes beyond
+ *                 448 (infinities included) saturate to +-448; NaN gives
+ *                 0x7F; zero keeps its sign.
+ * A token that two ranks own is written on both. Two tokens with the same
+ * valid slot on one rank race: which row lands is unspecified.
+ *
+ * k_new      device, [num_tokens, num_kv_heads, head_dim_k], contiguous,
+ *            src_dtype (DCP_F32 or DCP_BF16), 16-byte aligned
+ * v_new      device, [num_tokens, num_kv_heads, head_dim_v], like k_new;
+ *            must be NULL exactly when kv->v is NULL (MLA: the value is the
+ *            first head_dim_v entries of the K row, written with it)
+ * num_tokens >= 0 (0: nothing is launched)
+ * slots      device, [num_ranks, num_tokens] int64 (as from dcp_slot_mapping)
+ * num_ranks  1..64: pools kv describes, counted from the pool kv->k points to
+ * kv         the pools to write (k and v are written through despite the
+ *            const in dcp_kv_cache_t); head_dim_k and head_dim_v multiples
+ *            of 8; fp8 needs k_scale (and v_scale when v != NULL)
+ * Errors: DCP_ERR_INVALID_ARG (sizes, NULL pointers, v_new / kv->v mismatch,
+ * fp8 without scales), DCP_ERR_UNSUPPORTED (src_dtype, head dims not
+ * multiples of 8, num_ranks > 64, unaligned sources), DCP_ERR_HIP.
+ */
+int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, int64_t num_tokens,
+                       const int64_t* slots, int32_t num_ranks, const dcp_kv_cache_t* kv, void* stream);
+
+/*
  * Measurement hook for benchmarks.
  *
  * dcp_profile_enable(1) makes every following dcp_partial_decode_attn call

@@ -4,7 +4,7 @@ integer reference).
 Test infrastructure: see the package docstring.
 
 Sources: "Decode Context Parallel (DCP)" (vLLM Ascend developer guide),
-section "DCP slot mapping" (each rank stores only its local shard, at the slot
+section "KV-cache layout" (each rank stores only its local shard, at the slot
 the slot mapping gives); "DeepSeek V4.1 context parallelism" (TokenSpeed design
 note), section "Cache ownership" (a write turns the virtual slot into the
 owner's local slot and non-owners are masked). The pages fix the stored fp8
@@ -93,7 +93,9 @@ def store_values(x, fmt: str, scale=None) -> np.ndarray:
         return round_bf16_bits(x)
     if fmt == formats.FP8_E4M3:
         s = np.asarray(scale, dtype=np.float32).reshape([1] * (x.ndim - 2) + [-1, 1])
-        return quantize_e4m3fn((x / s).astype(np.float32))
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):  # IEEE results are wanted
+            q = (x / s).astype(np.float32)
+        return quantize_e4m3fn(q)
     raise ValueError(f"unknown stored format {fmt!r}")
 
 

@@ -235,6 +235,28 @@ int dcp_profile_collect(double* total_ms, int32_t* launches) {
   return DCP_OK;
 }
 
+int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, int64_t num_tokens,
+                       const int64_t* slots, int32_t num_ranks, const dcp_kv_cache_t* kv, void* stream) {
+  if (!kv || num_tokens < 0 || num_ranks < 1) return DCP_ERR_INVALID_ARG;
+  if (src_dtype != DCP_F32 && src_dtype != DCP_BF16) return DCP_ERR_UNSUPPORTED;
+  if (!valid_dtype(kv->dtype)) return DCP_ERR_UNSUPPORTED;
+  if (num_ranks > 64) return DCP_ERR_UNSUPPORTED;
+  if (kv->num_kv_heads < 1 || kv->block_size < 1 || kv->num_blocks < 1) return DCP_ERR_INVALID_ARG;
+  if (kv->head_dim_k < 1 || kv->head_dim_v < 1) return DCP_ERR_INVALID_ARG;
+  if ((v_new == nullptr) != (kv->v == nullptr)) return DCP_ERR_INVALID_ARG;
+  if (!kv->v && kv->head_dim_v > kv->head_dim_k) return DCP_ERR_INVALID_ARG;
+  if (kv->head_dim_k % 8 != 0 || (kv->v && kv->head_dim_v % 8 != 0)) return DCP_ERR_UNSUPPORTED;
+  if (int64_t(kv->num_kv_heads) * (kv->head_dim_k + kv->head_dim_v) > (int64_t(1) << 24)) return DCP_ERR_UNSUPPORTED;
+  if (kv->dtype == DCP_FP8_E4M3 && (!kv->k_scale || (kv->v && !kv->v_scale))) return DCP_ERR_INVALID_ARG;
+  if (num_tokens > (int64_t(1) << 33)) return DCP_ERR_INVALID_ARG;
+  if (num_tokens == 0) return DCP_OK;
+  if (!k_new || !slots || !kv->k) return DCP_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)
+    return DCP_ERR_UNSUPPORTED;
+  return launch_kv_write(k_new, v_new, src_dtype == DCP_BF16, num_tokens, slots, num_ranks, *kv,
+                         static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
 int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts, int32_t batch, int32_t num_heads,
                   int32_t head_dim_v, const float* sink, int32_t out_dtype, void* out_o, float* out_lse,
                   void* stream) {

@@ -23,6 +23,7 @@ TORCH_TO_DCP = {torch.float32: DCP_F32, torch.bfloat16: DCP_BF16, torch.float8_e
 EXPORTS = [
     "dcp_abi_version", "dcp_status_string", "dcp_local_seq_lens", "dcp_slot_mapping",
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
+    "dcp_kv_cache_write",
     "dcp_profile_enable", "dcp_profile_collect",
 ]
 
@@ -72,6 +73,8 @@ def lib():
                                               i32, i32, f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.dcp_lse_merge.restype = ctypes.c_int
         L.dcp_lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+        L.dcp_kv_cache_write.restype = ctypes.c_int
+        L.dcp_kv_cache_write.argtypes = [vp, vp, i32, i64, vp, i32, ctypes.POINTER(KvCache), vp]
         L.dcp_profile_enable.restype = ctypes.c_int
         L.dcp_profile_enable.argtypes = [ctypes.c_int]
         L.dcp_profile_collect.restype = ctypes.c_int
@@ -177,6 +180,21 @@ def dcp_lse_merge(part_o, part_lse, sink=None, out_dtype=torch.float32, out_o=No
         _ptr(part_o), _ptr(part_lse), R, B, H, Dv, _ptr(sink), TORCH_TO_DCP[out_o.dtype], _ptr(out_o),
         _ptr(out_lse), _stream(stream)))
     return out_o, out_lse
+
+
+def dcp_kv_cache_write(k_new, v_new, slots, kv: KvCache, stream=None):
+    """Store ``k_new [T, Hkv, Dk]`` (and ``v_new [T, Hkv, Dv]``, or None for MLA)
+    at ``slots [R, T]`` (int64, -1 = not on that rank) of the pools ``kv``
+    describes; R pools counted from ``kv.k``."""
+    assert k_new.is_contiguous() and k_new.dtype in (torch.float32, torch.bfloat16)
+    assert slots.dtype == torch.int64 and slots.is_contiguous() and slots.dim() == 2
+    if v_new is not None:
+        assert v_new.is_contiguous() and v_new.dtype == k_new.dtype and v_new.shape[0] == k_new.shape[0]
+    R, T = slots.shape
+    assert k_new.shape[0] == T
+    _check("dcp_kv_cache_write", lib().dcp_kv_cache_write(
+        _ptr(k_new), _ptr(v_new), TORCH_TO_DCP[k_new.dtype], T, _ptr(slots), R, ctypes.byref(kv),
+        _stream(stream)))
 
 
 def dcp_profile_enable(on: bool = True):

@@ -143,3 +143,29 @@ def test_merge_validation(L):
     assert f(p, p, 2, 2, 4, 8, NULL, 2, p, p, NULL) == UNS      # fp8 output
     assert f(NULL, p, 2, 2, 4, 8, NULL, 0, p, p, NULL) == INV
     assert f(NULL, NULL, 2, 0, 4, 8, NULL, 0, NULL, NULL, NULL) == 0
+
+
+def test_kv_cache_write_validation(L):
+    p = _fake(64)
+    f = L.dcp_kv_cache_write
+    F32, BF16 = native.DCP_F32, native.DCP_BF16
+
+    def call(k=p, v=p, src=BF16, T=4, slots=p, R=2, kv=None):
+        return f(k, v, src, T, slots, R, ctypes.byref(kv if kv is not None else _kv()), NULL)
+
+    assert call(T=-1) == INV
+    assert call(R=0) == INV
+    assert call(R=65) == UNS                                   # one lane per rank
+    assert call(src=native.DCP_FP8_E4M3) == UNS                # sources are fp32 or bf16
+    assert call(kv=_kv(dtype=9)) == UNS
+    assert call(v=NULL) == INV                                 # GQA pools need V rows
+    assert call(kv=_kv(v=None, head_dim_v=64)) == INV          # MLA pools take no V rows
+    assert call(kv=_kv(head_dim_k=100, head_dim_v=100)) == UNS # not a multiple of 8
+    assert call(kv=_kv(dtype=native.DCP_FP8_E4M3)) == INV      # fp8 without scales
+    assert call(kv=_kv(dtype=native.DCP_FP8_E4M3, k_scale=4096)) == INV  # V scale missing
+    assert call(kv=_kv(num_blocks=0)) == INV
+    assert call(k=NULL) == INV
+    assert call(slots=NULL) == INV
+    assert call(k=ctypes.c_void_p(p.value + 2)) == UNS         # unaligned source rows
+    assert call(T=0, k=NULL, slots=NULL) == 0                  # empty: nothing launched
+    assert call(T=0, src=F32, kv=_kv(v=None, head_dim_v=64), v=NULL) == 0

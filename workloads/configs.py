@@ -1,4 +1,5 @@
-"""The five synthetic decode workloads, named by what they are.
+"""The five synthetic decode workloads and the two KV-cache write workloads,
+named by what they are.
 
 Length laws ("k" = 1024 tokens):
 * ``loguniform(a, b)``: L = floor(exp(U(ln a, ln b))), clipped to [a, b];
@@ -94,3 +95,61 @@ def get_workload(name: str) -> Workload:
     if name not in WORKLOADS:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
     return WORKLOADS[name]
+
+
+@dataclass(frozen=True)
+class KvWriteWorkload:
+    """New tokens written into the pools of a decode workload's geometry:
+    ``requests`` requests each append ``chunk`` consecutive tokens after an
+    existing context of ``uniform(0, max_context)`` tokens (a chunked-prefill
+    step; ``chunk = 1`` is a decode step)."""
+    name: str
+    seed: int
+    base: str                 # decode workload giving format, heads, dims, block size, DCP layout
+    requests: int
+    chunk: int
+    max_context: int
+    src_format: str           # "fp32" | "bf16": format of the new rows
+    description: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.requests * self.chunk
+
+    def geometry(self) -> Workload:
+        return WORKLOADS[self.base]
+
+    def bytes_per_token(self) -> int:
+        """Algorithmic HBM bytes per token: new rows read, one slot per rank
+        read, stored rows written once (one owner)."""
+        g = self.geometry()
+        dims = g.head_dim_k if g.mla else g.head_dim_k + g.head_dim_v
+        src = {"fp32": 4, "bf16": 2}[self.src_format]
+        dst = {"fp32": 4, "bf16": 2, "fp8_e4m3": 1}[g.kv_format]
+        return g.num_kv_heads * dims * (src + dst) + 8 * g.dcp_size
+
+
+KV_WRITE_WORKLOADS = {
+    w.name: w
+    for w in [
+        KvWriteWorkload(
+            name="kvw_gqa_fp8_chunk", seed=11, base="gqa_fp8_binned", requests=32, chunk=2048,
+            max_context=16 * K, src_format="bf16",
+            description="GQA fp8 pools (8 KV heads x 128, per-head scales), 32 requests x 2048-token "
+                        "prefill chunks, bf16 rows"),
+        KvWriteWorkload(
+            name="kvw_mla_bf16_chunk", seed=12, base="mla_bf16_bimodal", requests=32, chunk=2048,
+            max_context=16 * K, src_format="bf16",
+            description="MLA bf16 latent pools (1 x 576), 32 requests x 2048-token prefill chunks, bf16 rows"),
+        KvWriteWorkload(
+            name="kvw_gqa_fp8_decode", seed=13, base="gqa_fp8_binned", requests=256, chunk=1,
+            max_context=256 * K, src_format="bf16",
+            description="one decode step's writes: 256 requests x 1 new token into GQA fp8 pools"),
+    ]
+}
+
+
+def get_kv_write_workload(name: str) -> KvWriteWorkload:
+    if name not in KV_WRITE_WORKLOADS:
+        raise KeyError(f"unknown KV-write workload {name!r}; known: {sorted(KV_WRITE_WORKLOADS)}")
+    return KV_WRITE_WORKLOADS[name]

@@ -27,9 +27,9 @@ import math
 import numpy as np
 import torch
 
-from .configs import Workload
+from .configs import KvWriteWorkload, Workload
 
-LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES = range(7)
+LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES, CONTEXT = range(8)
 
 TORCH_FORMAT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
 
@@ -181,3 +181,38 @@ def stored_numpy(t: torch.Tensor) -> np.ndarray:
 
 def stored_format(t: torch.Tensor) -> str:
     return {torch.float32: "fp32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8_e4m3"}[t.dtype]
+
+
+@dataclass
+class KvWriteCase:
+    workload: KvWriteWorkload
+    context: np.ndarray           # [requests] int64: tokens already in each request's cache
+    positions: np.ndarray         # [T] int64, request-major: context[b] .. context[b] + chunk - 1
+    req_indices: np.ndarray       # [T] int32
+    block_table: np.ndarray       # [requests, max_vblocks] int32 covering context + chunk
+    num_blocks: int               # physical blocks per rank pool
+    k_new: torch.Tensor           # [T, Hkv, Dk] in src_format
+    v_new: torch.Tensor           # [T, Hkv, Dv] in src_format, or None (MLA)
+    k_scale: np.ndarray           # [Hkv] float32 (fp8 pools) or None
+    v_scale: np.ndarray           # [Hkv] float32 (fp8 pools, GQA) or None
+
+
+def make_kv_write_case(w: KvWriteWorkload, device="cpu") -> KvWriteCase:
+    """Seeded new rows ~ N(0, 1) (rounded to ``src_format``) at the positions
+    right after each request's context; the block table, scales and pool
+    geometry follow the base decode workload's laws (stream 7 = contexts)."""
+    g = w.geometry()
+    ctx = _rng(w.seed, CONTEXT).integers(0, w.max_context + 1, size=w.requests).astype(np.int64)
+    table, num_blocks = make_block_table(g, (ctx + w.chunk).astype(np.int64))
+    positions = (ctx[:, None] + np.arange(w.chunk, dtype=np.int64)[None, :]).reshape(-1)
+    reqs = np.repeat(np.arange(w.requests, dtype=np.int32), w.chunk)
+    T = w.tokens
+    src = TORCH_FORMAT[w.src_format]
+    k_new = _randn((T, g.num_kv_heads, g.head_dim_k), _seed(w.seed, KSTREAM), device).to(src)
+    v_new = None
+    if not g.mla:
+        v_new = _randn((T, g.num_kv_heads, g.head_dim_v), _seed(w.seed, VSTREAM), device).to(src)
+    fp8 = g.kv_format == "fp8_e4m3"
+    k_scale = _scales(g, 0) if fp8 else None
+    v_scale = _scales(g, 1) if fp8 and not g.mla else None
+    return KvWriteCase(w, ctx, positions, reqs, table, num_blocks, k_new, v_new, k_scale, v_scale)
