@@ -273,7 +273,8 @@ int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts,
  *            of 8; fp8 needs k_scale (and v_scale when v != NULL)
  * Errors: DCP_ERR_INVALID_ARG (sizes, NULL pointers, v_new / kv->v mismatch,
  * fp8 without scales), DCP_ERR_UNSUPPORTED (src_dtype, head dims not
- * multiples of 8, num_ranks > 64, unaligned sources), DCP_ERR_HIP.
+ * multiples of 8 or head_dim_k + head_dim_v over 8192, num_ranks > 64,
+ * num_kv_heads > 65535, unaligned sources), DCP_ERR_HIP.
  */
 int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, int64_t num_tokens,
                        const int64_t* slots, int32_t num_ranks, const dcp_kv_cache_t* kv, void* stream);

@@ -247,8 +247,12 @@ int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, 
   if (!kv->v && kv->head_dim_v > kv->head_dim_k) return DCP_ERR_INVALID_ARG;
   if (kv->head_dim_k % 8 != 0 || (kv->v && kv->head_dim_v % 8 != 0)) return DCP_ERR_UNSUPPORTED;
   if (int64_t(kv->num_kv_heads) * (kv->head_dim_k + kv->head_dim_v) > (int64_t(1) << 24)) return DCP_ERR_UNSUPPORTED;
+  if (kv->num_kv_heads > 65535) return DCP_ERR_UNSUPPORTED;  // one grid row per head
+  if (kv->head_dim_k + (kv->v ? kv->head_dim_v : 0) > 8192) return DCP_ERR_UNSUPPORTED;
+  if (int64_t(kv->num_blocks) * kv->block_size >= (int64_t(1) << 56)) return DCP_ERR_UNSUPPORTED;
   if (kv->dtype == DCP_FP8_E4M3 && (!kv->k_scale || (kv->v && !kv->v_scale))) return DCP_ERR_INVALID_ARG;
   if (num_tokens > (int64_t(1) << 33)) return DCP_ERR_INVALID_ARG;
+  if (num_tokens * kv->num_kv_heads >= (int64_t(1) << 33)) return DCP_ERR_UNSUPPORTED;  // grid size
   if (num_tokens == 0) return DCP_OK;
   if (!k_new || !slots || !kv->k) return DCP_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(k_new) % 16 != 0 || reinterpret_cast<uintptr_t>(v_new) % 16 != 0)

@@ -131,12 +131,16 @@ def _slots_for(rng, T, R, N, bs, I):
     return slots
 
 
+# Batches under 1024 tokens take the per-(token, head) kernel, larger ones the
+# 64-token tile kernel (whose last tile is ragged in the cases below).
 GQA_CASES = [
     # (H, Dk, Dv, bs, R, I, N, T)
     (2, 16, 16, 16, 4, 1, 6, 70),
     (8, 128, 128, 16, 4, 2, 5, 150),
     (3, 24, 40, 8, 3, 8, 7, 65),
     (1, 8, 8, 1, 2, 1, 40, 33),
+    (2, 16, 16, 16, 4, 1, 80, 1100),
+    (3, 24, 136, 8, 3, 8, 150, 1030),
 ]
 
 
@@ -186,9 +190,10 @@ def test_gqa_write_bitexact(device, fmt, src, case, v_layout):
 
 @pytest.mark.parametrize("fmt", ["fp32", "bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("src", ["fp32", "bf16"])
-def test_mla_write_bitexact(device, fmt, src):
-    H, Dk, Dv, bs, R, I, N, T = 1, 576, 512, 64, 8, 1, 4, 300
-    rng = np.random.default_rng(1000 + len(fmt) + len(src))
+@pytest.mark.parametrize("N,T", [(4, 300), (7, 1500)])
+def test_mla_write_bitexact(device, fmt, src, N, T):
+    H, Dk, Dv, bs, R, I = 1, 576, 512, 64, 8, 1
+    rng = np.random.default_rng(1000 + len(fmt) + len(src) + T)
     slots = _slots_for(rng, T, R, N, bs, I)
     k32 = _special_values(rng, T * H * Dk).reshape(T, H, Dk)
     k_src = torch.from_numpy(k32).to(device).to(SRC_T[src])
@@ -202,6 +207,58 @@ def test_mla_write_bitexact(device, fmt, src):
     ocache.cache_write(ko, None, _oracle_input(k_src), None, slots, bs, fmt, ks_np, None)
     nb = {"fp32": np.uint32, "bf16": np.uint16, "fp8_e4m3": np.uint8}[fmt]
     assert np.array_equal(_host_bits(k_store), ko.view(nb))
+
+
+@pytest.mark.parametrize("reps", [1, 400])
+def test_fp8_quotients_next_to_code_midpoints(device, reps):
+    """Inputs whose quotient by a non-power-of-two scale lands on, or one fp32
+    step either side of, a midpoint between E4M3 codes: the cases where a
+    quotient computed with an error of even one fp32 ulp rounds apart."""
+    scales = np.array([0.37, 0.0134, 3.3, 1e-3, 7.77e-7, 2.0 ** 99, 1e-35, 1.0], dtype=np.float32)
+    H, D, bs, R = scales.size, 256, 16, 1                                            # 2 x 126 midpoints fit in D
+    e4m3 = ofmt.e4m3fn_table()[:0x7F]
+    mids = ((e4m3[:-1] + e4m3[1:]) / 2).astype(np.float32)
+    with np.errstate(over="ignore"):
+        base = np.concatenate([mids, -mids]).astype(np.float32)[None, :] * scales[:, None]   # [H, 252]
+    x = np.stack([base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(-np.inf))])
+    k32 = np.pad(x, ((0, 0), (0, 0), (0, D - x.shape[2]))).astype(np.float32)         # [3, H, D]
+    k32 = np.ascontiguousarray(np.tile(k32, (reps, 1, 1)))
+    T = k32.shape[0]
+    N = (T + 16) // bs + 2
+    slots = (np.random.default_rng(reps).permutation(N * bs)[:T]).astype(np.int64)[None, :]
+    sc = torch.from_numpy(scales).to(device)
+    k_store, k_log = _sentinel_pool((R, N, H, bs, D), "fp8_e4m3", device)
+    d = _descriptor("fp8_e4m3", k_log, None, N, bs, H, D, D, sc, None)
+    dcp.dcp_kv_cache_write(torch.from_numpy(k32).to(device), None, torch.from_numpy(slots).to(device), d)
+    torch.cuda.synchronize()
+    ko = _oracle_pool((R, N, H, bs, D), "fp8_e4m3")
+    ocache.cache_write(ko, None, k32, None, slots, bs, "fp8_e4m3", scales, None)
+    assert np.array_equal(_host_bits(k_store), ko)
+
+
+@pytest.mark.parametrize("fmt,scale", [("fp8_e4m3", 1.0), ("fp8_e4m3", 0.37), ("bf16", None)])
+def test_conversion_sweep_over_fp32_patterns(device, fmt, scale):
+    """Every 97th fp32 bit pattern (44M values: all exponents, signs, NaN
+    payloads, infinities, subnormals) through the tile kernel, each stored
+    value compared with the oracle's."""
+    H, D, bs = 8, 128, 64
+    pats = np.arange(0, 1 << 32, 97, dtype=np.uint64).astype(np.uint32)
+    T = -(-pats.size // (H * D))
+    pats = np.pad(pats, (0, T * H * D - pats.size))
+    k32 = pats.view(np.float32).reshape(T, H, D)
+    N = -(-T // bs)
+    scales = None if scale is None else np.full(H, scale, dtype=np.float32)
+    sc = None if scales is None else torch.from_numpy(scales).to(device)
+    k_store, k_log = _sentinel_pool((1, N, H, bs, D), fmt, device)
+    d = _descriptor(fmt, k_log, None, N, bs, H, D, D, sc, None)
+    slots = torch.arange(T, dtype=torch.int64, device=device)[None, :]
+    dcp.dcp_kv_cache_write(torch.from_numpy(k32).to(device), None, slots, d)
+    torch.cuda.synchronize()
+    got = _host_bits(k_store)[0].transpose(0, 2, 1, 3).reshape(N * bs, H, D)[:T]    # token order
+    exp = ocache.store_values(k32, fmt, scales)
+    bad = np.flatnonzero(got.reshape(-1) != exp.reshape(-1))
+    assert bad.size == 0, (f"{bad.size} mismatches, e.g. x bits {pats[bad[:4]]}: got {got.reshape(-1)[bad[:4]]}, "
+                           f"oracle {exp.reshape(-1)[bad[:4]]}")
 
 
 def test_empty_write_launches_nothing(device):
