@@ -1,4 +1,5 @@
-"""Float64 decode attention: full softmax, per-rank partials, LSE merge.
+"""Float64 decode attention: full softmax, per-rank partials, LSE merge, and
+multi-token decode (speculative verification).
 
 Test infrastructure: see the package docstring.
 
@@ -13,7 +14,10 @@ Sources:
   section 5.4 (GQA: query heads share their group's KV head).
 * "DeepSeek V4.1 context parallelism", section "Decode computation": the
   attention sink is applied once, when the partial outputs are merged by
-  log-sum-exp.
+  log-sum-exp; decode and speculative (DSpark) verification share the decode
+  path, each rank attending the pages it owns.
+* "Efficient Decode Context Parallelism with vLLM for Long Context Workloads",
+  section 6 (MTP and speculative decoding on the DCP decode path).
 
 Because sharding plus a log-sum-exp merge is an exact identity, the reference
 result is plain softmax attention over the unsharded sequence. Readings where
@@ -25,7 +29,10 @@ the pages are silent:
   that joins the softmax denominator with a zero value vector;
 * an empty token set gives O = 0 and LSE = -inf (LSE = sink with a sink);
 * for MLA the value of a token is the first ``Dv`` entries of its stored key
-  row (latent part), so the caller passes ``v = k[..., :Dv]``.
+  row (latent part), so the caller passes ``v = k[..., :Dv]``;
+* multi-token decode: the ``q_len`` queried tokens are the last ``q_len``
+  positions, already in the cache, and query ``i`` attends every position up
+  to its own (``verify_attention``).
 """
 
 import numpy as np
@@ -80,6 +87,40 @@ def rank_partials(q, k, v, scale: float, owner, dcp_size: int):
     owner = np.asarray(owner)
     parts = [decode_attention(q, k[owner == r], v[owner == r], scale) for r in range(dcp_size)]
     return np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
+
+
+def verify_attention(q, k, v, scale: float, sink=None):
+    """Multi-token decode (MTP / speculative verification), float64.
+
+    The last ``q_len`` tokens of a sequence are queried at once; their keys
+    and values are already in ``k [L, Hkv, Dk]`` / ``v [L, Hkv, Dv]``.
+    Query ``i`` (``q[i]``, ``[Hq, Dk]``) sits at position ``L - q_len + i``
+    and attends positions ``0 .. L - q_len + i`` (causal among the new
+    tokens; the earlier context is seen in full). Returns
+    ``(O [q_len, Hq, Dv], LSE [q_len, Hq])``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    q_len, L = q.shape[0], k.shape[0]
+    if q_len > L:
+        raise ValueError("the queried tokens must be in the cache (q_len <= L)")
+    res = [decode_attention(q[i], k[:L - q_len + i + 1], v[:L - q_len + i + 1], scale, sink) for i in range(q_len)]
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
+
+
+def verify_rank_partials(q, k, v, scale: float, owner, dcp_size: int):
+    """Per-rank partials of multi-token decode: for query ``i``, rank ``r``
+    attends the tokens it owns at positions ``<= L - q_len + i``.
+    Returns ``(O [D, q_len, Hq, Dv], LSE [D, q_len, Hq])``."""
+    q = np.asarray(q, dtype=np.float64)
+    owner = np.asarray(owner)
+    q_len, L = q.shape[0], k.shape[0]
+    os_, ls_ = [], []
+    for i in range(q_len):
+        seen = slice(0, L - q_len + i + 1)
+        o, lse = rank_partials(q[i], k[seen], v[seen], scale, owner[seen], dcp_size)
+        os_.append(o)
+        ls_.append(lse)
+    return np.stack(os_, axis=1), np.stack(ls_, axis=1)
 
 
 def lse_merge(part_o, part_lse, sink=None):
