@@ -17,6 +17,11 @@ distributions of the named workload). Prints ONE JSON line:
 * ``cpu_baseline`` - the float64 CPU oracle timed on a bounded sample of the
                 same batch (rank 0, N = 1 only).
 
+With a multi-token decode workload (``--workload *_q<N>``) a step is every
+rank's partial attention for the last N tokens of every request at once
+(causal among them) plus the merge; ``value`` counts the KV bytes of the
+batch once, like decode, and ``config`` adds the verified tokens per second.
+
 With ``--workload kvw_*`` a step is instead the KV-cache write of a batch of
 new tokens (slot mapping, then the write of every row into its owner's pool);
 ``value`` and ``roofline`` then count the write's algorithmic bytes (new rows
@@ -39,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU"
 DEFAULT_WORKLOAD = "gqa_fp8_binned"
 KV_WRITE_METRIC = "KV-cache write GB/s (new rows + slots read, stored rows written) at 1 GPU"
+VERIFY_METRIC = "multi-token decode KV GB/s (% of MI355X HBM peak) + verified tokens/s at 1 GPU"
 KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
                 "kv_write": "kv_write"}
 KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip",
@@ -72,17 +78,22 @@ def load_traffic(family, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def blas_threads():
+    """Threads NumPy's BLAS uses (the oracle's matrix products run there)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing
+        return 1
+
+
 def cpu_baseline(case, budget_s):
     """Time the float64 oracle on a seeded sample of requests (~budget_s)."""
     import numpy as np
     from oracle import attention as oatt
     from oracle import formats as ofmt
     from workloads.generate import stored_format, stored_numpy
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing
-        threads = 1
+    threads = blas_threads()
     w = case.workload
     order = np.random.default_rng(12345).permutation(case.batch)
     spent, kv_bytes, done = 0.0, 0, []
@@ -263,6 +274,122 @@ def bench_kv_write(args, name):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_verify(case, q, q_len, budget_s):
+    """Time the float64 oracle's multi-token decode on a seeded sample of requests."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import formats as ofmt
+    from workloads.generate import stored_format, stored_numpy
+    w = case.workload
+    qh = q.cpu()
+    order = np.random.default_rng(12345).permutation(case.batch)
+    spent, kv_bytes, done = 0.0, 0, []
+    for b in order:
+        q_st = stored_numpy(qh[b])
+        k_st = stored_numpy(case.k[b])
+        v_st = None if case.v is None else stored_numpy(case.v[b])
+        t0 = time.perf_counter()
+        qq = ofmt.decode(q_st, stored_format(qh))
+        k = ofmt.decode_kv(k_st, stored_format(case.k[b]), case.k_scale)
+        v = k[:, :, :w.head_dim_v] if v_st is None else ofmt.decode_kv(v_st, stored_format(case.v[b]), case.v_scale)
+        oatt.verify_attention(qq, k, v, w.softmax_scale, case.sink)
+        spent += time.perf_counter() - t0
+        kv_bytes += int(case.seq_lens[b]) * w.kv_bytes_per_token()
+        done.append(int(b))
+        if spent >= budget_s:
+            break
+    return {
+        "value": kv_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads()),
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {case.batch} requests ({q_len} query tokens each, seeded random order), "
+                   f"causal attention per query token over the unsharded sequence in float64 incl. decoding the "
+                   f"stored KV; {spent:.1f} s"),
+        "verified_tokens_per_s": len(done) * q_len / spent,
+    }
+
+
+def bench_verify(args, vw):
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from tests.harness import DeviceInputs, VerifyRun
+    from workloads import make_case, make_verify_queries
+
+    w = vw.geometry()
+    t_gen = time.perf_counter()
+    case = make_case(w, device="cuda")
+    inp = DeviceInputs(case, "cuda", fill="zero")
+    q = make_verify_queries(w, case.batch, vw.q_len, "cuda")
+    run = VerifyRun(inp, q, algo=dcp.DCP_ALGO_AUTO)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {vw.name}: batch {case.batch} x {vw.q_len} query tokens, {int(case.seq_lens.sum())} tokens, "
+          f"{case.kv_bytes() / 1e9:.3f} GB KV, inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dcp.native.dcp_profile_enable(True)
+    dcp.native.dcp_profile_collect()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        run.step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern_ms, launches = dcp.native.dcp_profile_collect()
+    dcp.native.dcp_profile_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    kern_avg_ms = kern_ms / max(launches, 1)
+    kv_bytes = case.kv_bytes()
+    family = kernel_family(w)
+    out = {
+        "metric": VERIFY_METRIC,
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": vw.name,
+            "base": w.name,
+            "q_len": vw.q_len,
+            "batch": case.batch,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "kv_format": w.kv_format,
+            "dcp_size": w.dcp_size,
+            "interleave": w.interleave,
+            "tokens": int(case.seq_lens.astype(np.int64).sum()),
+            "kv_bytes": int(kv_bytes),
+            "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "verified_tokens_per_s": round(case.batch * vw.q_len / (ms * 1e-3), 1),
+            "kernel": KERNEL_NAMES[family],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(kv_bytes / (kern_avg_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kv_bytes / (kern_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(family, vw.name),
+            "kernel_avg_ms": round(kern_avg_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_verify(case, q, vw.q_len, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +433,10 @@ def main():
         return
     if args.workload.startswith("kvw_"):
         bench_kv_write(args, args.workload)
+        return
+    from workloads import VERIFY_WORKLOADS
+    if args.workload in VERIFY_WORKLOADS:
+        bench_verify(args, VERIFY_WORKLOADS[args.workload])
         return
     w = get_workload(args.workload)
     t_gen = time.perf_counter()

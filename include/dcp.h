@@ -204,6 +204,55 @@ int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32
                             size_t workspace_bytes, void* stream);
 
 /*
+ * dcp_partial_verify_attn - each rank's partial attention for several new
+ * tokens of every request at once (multi-token decode: MTP, speculative
+ * verification), causal among them.
+ *
+ * Source: "DeepSeek V4.1 context parallelism", section "Decode computation"
+ * (decode and speculative verification share the decode path: each rank
+ * attends the pages it owns); "Efficient Decode Context Parallelism with vLLM
+ * for Long Context Workloads", section 6 (MTP and speculative decoding on the
+ * DCP decode path); "Decode Context Parallel (DCP)", section "Decode".
+ *
+ * The last q_len tokens of request b (already written to the cache, e.g. by
+ * dcp_kv_cache_write) are queried together: query token i sits at position
+ * L_b - q_len + i and attends every cached position up to its own. Its
+ * rank-local tokens are the first n(b, i, r) local tokens of rank r's shard
+ * (local order is ascending position), n = local_lens[(b * q_len + i) *
+ * dcp_size + rank_begin + r], which is what dcp_local_seq_lens returns for
+ * the sequence length L_b - q_len + i + 1. With those lengths, for rank r,
+ * query token i, query head h (KV head g = h / (num_q_heads / num_kv_heads)):
+ *   s_j   = softmax_scale * <q[b,i,h,:], k_j[g,:]>, j < n(b, i, r)
+ *   LSE   = ln sum_j exp(s_j)                       (-inf when n == 0)
+ *   O     = sum_j exp(s_j - LSE) * v_j[g,:]         (0 when n == 0)
+ * (each row is the dcp_partial_decode_attn result for that query token and
+ * length; q_len = 1 is dcp_partial_decode_attn). Merging the rank partials
+ * with dcp_lse_merge (batch = batch * q_len) gives causal attention.
+ *
+ * q           device, [batch, q_len, num_q_heads, head_dim_k], contiguous
+ * q_len       1..64 query tokens per request
+ * local_lens  device, [batch, q_len, dcp_size] int32, each <= max_vblocks *
+ *             block_size
+ * out_o       device, [rank_count, batch, q_len, num_q_heads, head_dim_v] f32
+ * out_lse     device, [rank_count, batch, q_len, num_q_heads] f32
+ * other arguments and errors as for dcp_partial_decode_attn. The GQA MFMA
+ * kernel reads the KV once for up to 16 / (num_q_heads / num_kv_heads)
+ * query tokens of a request; the MLA MFMA kernel takes each query token
+ * separately.
+ */
+size_t dcp_partial_verify_attn_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads,
+                                              int32_t q_dtype, const dcp_kv_cache_t* kv,
+                                              int32_t rank_count, int32_t algo, int* status);
+
+int dcp_partial_verify_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q_len,
+                            int32_t num_q_heads, const dcp_kv_cache_t* kv,
+                            const int32_t* block_table, int64_t block_table_stride,
+                            int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size,
+                            int32_t rank_begin, int32_t rank_count, float softmax_scale,
+                            int32_t algo, float* out_o, float* out_lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * dcp_lse_merge - combine per-rank partials into exact attention, applying an
  * attention sink once.
  *
@@ -282,8 +331,9 @@ int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, 
 /*
  * Measurement hook for benchmarks.
  *
- * dcp_profile_enable(1) makes every following dcp_partial_decode_attn call
- * made by this host thread record a pair of HIP events on its stream, right
+ * dcp_profile_enable(1) makes every following dcp_partial_decode_attn and
+ * dcp_partial_verify_attn call made by this host thread record a pair of HIP
+ * events on its stream, right
  * before and right after its main attention kernel (the planner and the split
  * combine are outside the pair). dcp_profile_collect waits for the recorded
  * events, returns the summed elapsed milliseconds and the number of calls

@@ -1,5 +1,6 @@
 // C ABI entry points of libdcp: host-side validation, kernel selection and
 // launch. The operations and their sources are documented in include/dcp.h.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <utility>
@@ -35,10 +36,13 @@ static bool valid_dtype(int32_t t) { return t == DCP_F32 || t == DCP_BF16 || t =
 
 // Validation shared by the size query and the launch. Fills p (except the
 // output, workspace and stream fields) and picks the kernel family.
-static int validate_attn(int32_t batch, int32_t num_q_heads, int32_t q_dtype, const dcp_kv_cache_t* kv,
-                         int32_t rank_count, int32_t algo, AttnParams& p, AttnKernel& kernel) {
+static int validate_attn(int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t q_dtype,
+                         const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo, AttnParams& p,
+                         AttnKernel& kernel) {
   if (!kv) return DCP_ERR_INVALID_ARG;
   if (batch < 0 || num_q_heads < 1 || rank_count < 1) return DCP_ERR_INVALID_ARG;
+  if (q_len < 1 || q_len > 64) return DCP_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(batch) * q_len >= (int64_t(1) << 31)) return DCP_ERR_INVALID_ARG;
   if (q_dtype != DCP_F32 && q_dtype != DCP_BF16) return DCP_ERR_UNSUPPORTED;
   if (!valid_dtype(kv->dtype)) return DCP_ERR_UNSUPPORTED;
   if (kv->num_kv_heads < 1 || num_q_heads % kv->num_kv_heads != 0) return DCP_ERR_INVALID_ARG;
@@ -54,10 +58,21 @@ static int validate_attn(int32_t batch, int32_t num_q_heads, int32_t q_dtype, co
   p.group = num_q_heads / kv->num_kv_heads;
   p.kv = *kv;
   p.rank_count = rank_count;
+  p.q_len = q_len;
+  // GQA MFMA: the query tokens of a request share the 16 columns of the
+  // score tile (16 / group of them per unit); MLA MFMA: one per unit.
+  auto tokens_per_unit = [&](int tpu) {
+    p.tpu = tpu;
+    p.ntg = (q_len + tpu - 1) / tpu;
+  };
+  tokens_per_unit(std::max(1, std::min(q_len, 16 / std::max(1, p.group))));
+  if (algo != DCP_ALGO_GENERIC && gqa_supported(p)) {
+    kernel = AttnKernel::GqaMfma;
+    return DCP_OK;
+  }
+  tokens_per_unit(1);
   if (algo == DCP_ALGO_GENERIC) {
     kernel = AttnKernel::Generic;
-  } else if (gqa_supported(p)) {
-    kernel = AttnKernel::GqaMfma;
   } else if (mla_supported(p)) {
     kernel = AttnKernel::MlaMfma;
   } else if (algo == DCP_ALGO_FAST) {
@@ -161,25 +176,28 @@ int dcp_slot_mapping(const int64_t* positions, const int32_t* req_indices, int64
                              static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
 }
 
-size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
-                                              const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo,
-                                              int* status) {
+}  // extern "C"
+
+namespace dcp {
+
+static size_t attn_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t q_dtype,
+                                  const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo, int* status) {
   AttnParams p{};
   AttnKernel k = AttnKernel::Generic;
-  const int st = validate_attn(batch, num_q_heads, q_dtype, kv, rank_count, algo, p, k);
+  const int st = validate_attn(batch, q_len, num_q_heads, q_dtype, kv, rank_count, algo, p, k);
   if (status) *status = st;
   if (st != DCP_OK) return 0;
   return workspace_for(p, k);
 }
 
-int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
-                            const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
-                            int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
-                            int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q_len, int32_t num_q_heads,
+                        const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
+                        int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
+                        int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   AttnParams p{};
   AttnKernel k = AttnKernel::Generic;
-  if (int st = validate_attn(batch, num_q_heads, q_dtype, kv, rank_count, algo, p, k)) return st;
+  if (int st = validate_attn(batch, q_len, num_q_heads, q_dtype, kv, rank_count, algo, p, k)) return st;
   if (dcp_size < 1 || rank_begin < 0 || rank_begin + rank_count > dcp_size) return DCP_ERR_INVALID_ARG;
   if (max_vblocks < 0 || block_table_stride < max_vblocks) return DCP_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return DCP_ERR_INVALID_ARG;
@@ -211,6 +229,42 @@ int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32
     default: e = launch_generic_attn(p); break;
   }
   return e == hipSuccess ? DCP_OK : DCP_ERR_HIP;
+}
+
+}  // namespace dcp
+
+extern "C" {
+
+size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
+                                              const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo,
+                                              int* status) {
+  return attn_workspace_size(batch, 1, num_q_heads, q_dtype, kv, rank_count, algo, status);
+}
+
+int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                            const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
+                            int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
+                            int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return partial_attn(q, q_dtype, batch, 1, num_q_heads, kv, block_table, block_table_stride, max_vblocks,
+                      local_lens, dcp_size, rank_begin, rank_count, softmax_scale, algo, out_o, out_lse, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t dcp_partial_verify_attn_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t q_dtype,
+                                              const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo,
+                                              int* status) {
+  return attn_workspace_size(batch, q_len, num_q_heads, q_dtype, kv, rank_count, algo, status);
+}
+
+int dcp_partial_verify_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q_len, int32_t num_q_heads,
+                            const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
+                            int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
+                            int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return partial_attn(q, q_dtype, batch, q_len, num_q_heads, kv, block_table, block_table_stride, max_vblocks,
+                      local_lens, dcp_size, rank_begin, rank_count, softmax_scale, algo, out_o, out_lse, workspace,
+                      workspace_bytes, stream);
 }
 
 int dcp_profile_enable(int on) {

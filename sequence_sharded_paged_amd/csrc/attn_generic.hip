@@ -6,7 +6,8 @@
 //
 // This kernel serves the geometries the MFMA kernels do not (fp32 KV, other
 // head dims, other layouts) and cross-checks them. One workgroup per (rank,
-// request, query head) walks the rank's local tokens in chunks of 256: each
+// request, query token, query head) walks the local tokens that query sees in
+// chunks of 256: each
 // thread scores one token with an fp32 dot product, the workgroup updates the
 // running max and sum (online softmax), and each thread then accumulates its
 // output dimensions over the chunk. Every K/V element goes through the
@@ -31,18 +32,21 @@ __global__ void __launch_bounds__(kGenThreads) generic_attn_kernel(AttnParams p)
   __shared__ float q_s[kGenMaxDim];
   __shared__ float p_s[kGenThreads];
   __shared__ float red[kGenThreads / 64];
+  // one workgroup per (rank r, query row bq = b * q_len + i, query head h)
+  const int nq = p.batch * p.q_len;
   const int h = blockIdx.x % p.num_q_heads;
-  const int b = (blockIdx.x / p.num_q_heads) % p.batch;
-  const int r = blockIdx.x / (p.num_q_heads * p.batch);
+  const int bq = (blockIdx.x / p.num_q_heads) % nq;
+  const int r = blockIdx.x / (p.num_q_heads * nq);
+  const int b = bq / p.q_len;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = h / p.group;
   const dcp_kv_cache_t& kv = p.kv;
   const int Dk = kv.head_dim_k, Dv = kv.head_dim_v;
-  const int n = p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r];
-  const int64_t out_row = (static_cast<int64_t>(r) * p.batch + b) * p.num_q_heads + h;
+  const int n = max(p.local_lens[static_cast<int64_t>(bq) * p.dcp_size + p.rank_begin + r], 0);
+  const int64_t out_row = (static_cast<int64_t>(r) * nq + bq) * p.num_q_heads + h;
 
   for (int d = tid; d < Dk; d += kGenThreads) {
-    const int64_t qi = (static_cast<int64_t>(b) * p.num_q_heads + h) * Dk + d;
+    const int64_t qi = (static_cast<int64_t>(bq) * p.num_q_heads + h) * Dk + d;
     q_s[d] = (kQDtype == DCP_F32) ? reinterpret_cast<const float*>(p.q)[qi]
                                   : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qi]);
   }
@@ -126,7 +130,7 @@ static hipError_t launch_generic_q(const AttnParams& p, dim3 grid) {
 }
 
 hipError_t launch_generic_attn(const AttnParams& p) {
-  const int64_t n = static_cast<int64_t>(p.rank_count) * p.batch * p.num_q_heads;
+  const int64_t n = static_cast<int64_t>(p.rank_count) * p.batch * p.q_len * p.num_q_heads;
   if (n == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n));
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);

@@ -1,5 +1,6 @@
 // GQA per-rank partial decode attention on MFMA (bf16 or fp8-e4m3 KV, head
-// dim 128, up to 16 query heads per KV head).
+// dim 128, up to 16 (query token, query head) columns per KV head: a decode
+// query's group, or the groups of several query tokens of a request).
 //
 // Source: "Decode Context Parallel (DCP)" (vLLM Ascend design doc), section
 // "Decode" (attention of the gathered query heads against the local KV shard,
@@ -7,7 +8,8 @@
 // for Long Context Workloads", section 5.4 (the query heads of a group share
 // one KV head).
 //
-// Work split: stream-K over (rank, request, KV head) units (splitkv.h) with
+// Work split: stream-K over (rank, request, KV head, query tokens) units
+// (splitkv.h) with
 // one persistent wavefront per worker and tiles of TOK tokens (16 KB of K and
 // V per tile), streamed two tiles at a time straight into registers.
 //
@@ -139,9 +141,12 @@ __device__ __forceinline__ void gqa_issue(GqaBuf<kFp8>& B, GqaIds ids, int t, in
 }
 
 // Scores, online softmax and value product of one tile whose loads landed.
+// len: the unit's local tokens (the longest query's); col_len: tokens this
+// lane's column (query token, head) sees; min_len: the fewest any column sees.
 template <bool kFp8>
-__device__ __forceinline__ void gqa_tile(GqaBuf<kFp8>& B, int t0, int len, float c2, const bf16x8_t (&qop)[4],
-                                         f32x4_t (&o)[8], float& m_run, float& l_run, float& e_run, int qd) {
+__device__ __forceinline__ void gqa_tile(GqaBuf<kFp8>& B, int t0, int len, int col_len, int min_len, float c2,
+                                         const bf16x8_t (&qop)[4], f32x4_t (&o)[8], float& m_run, float& l_run,
+                                         float& e_run, int qd) {
   using C = GqaTile<kFp8>;
   constexpr int NT = C::NT, RUN = C::RUN;
   constexpr int EB = kFp8 ? 1 : 2;
@@ -168,12 +173,12 @@ __device__ __forceinline__ void gqa_tile(GqaBuf<kFp8>& B, int t0, int len, float
   // ---- online softmax (log2 domain) ----------------------------------
 #pragma unroll
   for (int ut = 0; ut < NT; ++ut) s[ut] *= c2;
-  if (t0 + C::TOK > len) {  // last tile of the shard (wave-uniform test)
+  if (t0 + C::TOK > min_len) {  // a tile some column sees only in part (wave-uniform test)
 #pragma unroll
     for (int ut = 0; ut < NT; ++ut)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (t0 + RUN * qd + 4 * ut + i >= len) s[ut][i] = -INFINITY;
+        if (t0 + RUN * qd + 4 * ut + i >= col_len) s[ut][i] = -INFINITY;
   }
   float mloc = -INFINITY;
 #pragma unroll
@@ -188,7 +193,8 @@ __device__ __forceinline__ void gqa_tile(GqaBuf<kFp8>& B, int t0, int len, float
   // enough in fp32 and bf16 alike. The decision is wave-uniform.
   if (__builtin_amdgcn_ballot_w64(mloc > m_run + kGqaRescaleLog2) != 0) {
     const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    // 0 on a column's first tile with tokens; 1 for a column that has seen none yet
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
     e_run *= alpha;
@@ -251,8 +257,8 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
   // tile quantity in scalar registers and the tile loop free of exec masks
   const int worker = __builtin_amdgcn_readfirstlane(blockIdx.x * kGqaWavesPerBlock + (threadIdx.x >> 6));
   const int n = lane & 15, qd = lane >> 4;
-  const int Hkv = p.kv.num_kv_heads, G = p.group;
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * Hkv;
+  const int G = p.group, rows = p.tpu * G;
+  const int64_t U = split_units(p);
   SplitWs ws = split_ws(p.workspace, U, kGqaMaxWorkers);
   const int64_t T = ws.prefix[U];
   if (worker >= workers || T == 0) return;
@@ -274,10 +280,19 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
     const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
     if (uend <= tile) { ++u; continue; }
     const int64_t t_lo = tile - ubeg, t_hi = min(wend, uend) - ubeg;  // unit-local tile range
-    const int h = static_cast<int>(u % Hkv);
-    const int64_t rb = u / Hkv;
-    const int b = static_cast<int>(rb % p.batch), r = static_cast<int>(rb / p.batch);
-    const int len = p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r];
+    const UnitRef x = unit_ref(p, u);
+    const int h = x.h, b = x.b, r = x.r;
+    // column n = (query token x.i0 + n / G, head g = n % G); columns past the
+    // unit's last query token have Q = 0 and the unit's length
+    const int qi = x.i0 + n / G;
+    const bool col = n < rows && qi < x.i1;
+    int len = 0, min_len = 0x7fffffff;
+    for (int i = x.i0; i < x.i1; ++i) {  // wave-uniform
+      const int li = query_len(p, b, i, r);
+      len = max(len, li);
+      min_len = min(min_len, li);
+    }
+    const int col_len = col ? query_len(p, b, qi, r) : len;
     const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
     const char* kh = kbase + (r * ks0 + h * ks2) * EB;
     const char* vh = vbase + (r * vs0 + h * vs2) * EB;
@@ -285,17 +300,17 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
     const float vscale = kFp8 ? p.kv.v_scale[h] : 1.f;
     const float c2 = p.softmax_scale * kscale * DCP_LOG2E;
 
-    // Q^T operand for the 4 k-steps over the 128 dims (zero for head >= G).
+    // Q^T operand for the 4 k-steps over the 128 dims (zero for unused columns).
     bf16x8_t qop[4];
     {
       const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) +
-                             (static_cast<int64_t>(b) * p.num_q_heads + h * G + n) * kGqaDim;
-      const uint16_t* qsrc = n < G ? qrow : reinterpret_cast<const uint16_t*>(p.q);  // in bounds, then zeroed
+                             ((static_cast<int64_t>(b) * p.q_len + qi) * p.num_q_heads + h * G + n % G) * kGqaDim;
+      const uint16_t* qsrc = col ? qrow : reinterpret_cast<const uint16_t*>(p.q);  // in bounds, then zeroed
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int d0 = kFp8 ? (64 * (k >> 1) + 16 * qd + 8 * (k & 1)) : (32 * k + 8 * qd);
         u32x4_t raw = ldg16(qsrc + d0);
-        if (n >= G) raw = u32x4_t{0u, 0u, 0u, 0u};
+        if (!col) raw = u32x4_t{0u, 0u, 0u, 0u};
         qop[k] = __builtin_bit_cast(bf16x8_t, raw);
       }
     }
@@ -326,8 +341,9 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
       gqa_issue<kFp8>(buf_b, ids_b, min(t + 1, t_last), len, bs, kh, ks1, ks3, vh, vs1, vs4, n, qd);
       ids_a = gqa_load_ids<kFp8>(bt, min(t + 2, t_last), len, bs, n, qd);
       ids_b = gqa_load_ids<kFp8>(bt, min(t + 3, t_last), len, bs, n, qd);
-      gqa_tile<kFp8>(buf_a, t * TOK, len, c2, qop, o, m_run, l_run, e_run, qd);
-      if (t + 1 < te) gqa_tile<kFp8>(buf_b, (t + 1) * TOK, len, c2, qop, o, m_run, l_run, e_run, qd);
+      gqa_tile<kFp8>(buf_a, t * TOK, len, col_len, min_len, c2, qop, o, m_run, l_run, e_run, qd);
+      if (t + 1 < te)
+        gqa_tile<kFp8>(buf_b, (t + 1) * TOK, len, col_len, min_len, c2, qop, o, m_run, l_run, e_run, qd);
     }
 
     // ---- piece end: full unit -> final output, else partial --------------
@@ -337,9 +353,9 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
     e_tot += __shfl_xor(e_tot, 32, 64);
     const bool whole = (t_lo == 0) && (t_hi == uend - ubeg);
     if (whole) {
-      const float inv = vscale / l_tot;
-      if (n < G) {
-        const int64_t row = (rb * p.num_q_heads + static_cast<int64_t>(h) * G + n);
+      const float inv = l_tot > 0.f ? vscale / l_tot : 0.f;  // l_tot = 0: the column sees no token (O = 0)
+      if (col) {
+        const int64_t row = out_row(p, x, qi, n % G);
         float* dst = p.out_o + row * kGqaDim;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
@@ -350,8 +366,8 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
       }
     } else {
       const int which = (t_lo == 0) ? 1 : 0;  // 0: unit began before this worker
-      float* dst = ws.part + ((static_cast<int64_t>(worker) * 2 + which) * G) * (kGqaDim + kPartExtra);
-      if (n < G) {
+      float* dst = ws.part + ((static_cast<int64_t>(worker) * 2 + which) * rows) * (kGqaDim + kPartExtra);
+      if (n < rows) {
         float* hrow = dst + static_cast<int64_t>(n) * (kGqaDim + kPartExtra);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
@@ -378,7 +394,7 @@ bool gqa_supported(const AttnParams& p) {
   if (p.q_dtype != DCP_BF16) return false;
   if (kv.dtype != DCP_BF16 && kv.dtype != DCP_FP8_E4M3) return false;
   if (kv.head_dim_k != kGqaDim || kv.head_dim_v != kGqaDim || !kv.v) return false;
-  if (p.group > 16) return false;
+  if (p.tpu * p.group > 16) return false;  // (query token, head) columns of the 16-wide MFMA tile
   if (kv.block_size % 16 != 0) return false;
   if (kv.k_stride[4] != 1 || kv.v_stride[3] != 1) return false;
   const int eb = kv.dtype == DCP_BF16 ? 2 : 1;
@@ -392,8 +408,7 @@ bool gqa_supported(const AttnParams& p) {
 }
 
 size_t gqa_workspace_bytes(const AttnParams& p) {
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
-  return split_ws_bytes(U, kGqaMaxWorkers, p.group, kGqaDim);
+  return split_ws_bytes(split_units_host(p), kGqaMaxWorkers, p.tpu * p.group, kGqaDim);
 }
 
 template <bool kFp8>

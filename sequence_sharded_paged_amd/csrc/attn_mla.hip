@@ -13,7 +13,8 @@
 // design goal is to keep the matrix cores busy, and everything else (LDS
 // operand reads, softmax, address arithmetic) runs in their shadow.
 //
-// Work split: stream-K over (rank, request) units (splitkv.h), one persistent
+// Work split: stream-K over (rank, request, query token) units (splitkv.h;
+// one query token per unit when several are decoded at once), one persistent
 // 256-thread workgroup (one wavefront per SIMD) per worker, tiles of 32
 // tokens. Per workgroup:
 //   * a 4-stage LDS ring of 32-token tiles (36 KB each) is filled straight
@@ -221,8 +222,10 @@ mla_attn_kernel(AttnParams p, int workers) {
       w.fresh = true;
     }
     if (w.fresh) {
-      const int uu = static_cast<int>(w.u), b = uu % p.batch, r = uu / p.batch;
-      w.len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r);
+      // unit u = (r * batch + b) * q_len + i: rank r, request b, query token i
+      const int uu = static_cast<int>(w.u), rb = uu / p.q_len, i = uu - rb * p.q_len;
+      const int b = rb % p.batch, r = rb / p.batch;
+      w.len = ld_uniform(p.local_lens + (static_cast<int64_t>(b) * p.q_len + i) * p.dcp_size + p.rank_begin + r);
       w.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
       w.rk = kbase + r * ks0 * 2;
       const int t0 = static_cast<int>(w.t - w.ubeg) * kMlaTile;
@@ -364,9 +367,11 @@ mla_attn_kernel(AttnParams p, int workers) {
     while (ld_uniform(ws.prefix + cur_u + 1) <= tile) ++cur_u;
     const int64_t ubeg = ld_uniform(ws.prefix + cur_u), uend = ld_uniform(ws.prefix + cur_u + 1);
     const int64_t lt_lo = tile - ubeg, lt_hi = min(wend, uend) - ubeg;
-    const int b = static_cast<int>(cur_u % p.batch);
-    const int len = ld_uniform(p.local_lens + static_cast<int64_t>(b) * p.dcp_size + p.rank_begin +
-                               static_cast<int>(cur_u / p.batch));
+    const int64_t rb = cur_u / p.q_len;
+    const int qi = static_cast<int>(cur_u - rb * p.q_len);
+    const int b = static_cast<int>(rb % p.batch);
+    const int len = ld_uniform(p.local_lens + (static_cast<int64_t>(b) * p.q_len + qi) * p.dcp_size + p.rank_begin +
+                               static_cast<int>(rb / p.batch));
     const int64_t piece_tile0 = tile, piece_end = tile + (lt_hi - lt_lo);
 
     // Q operand (B of the score MFMA): head 32 wave + l % 32, dims 16 ks + 8 h
@@ -374,8 +379,8 @@ mla_attn_kernel(AttnParams p, int workers) {
     bf16x8_t qop[kMlaKStepsLat];
     {
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) +
-                           (static_cast<int64_t>(b) * kMlaHeads + kMlaHeadsPerWave * wave + (lane & 31)) * kMlaDk +
-                           8 * h;
+                           ((static_cast<int64_t>(b) * p.q_len + qi) * kMlaHeads + kMlaHeadsPerWave * wave +
+                            (lane & 31)) * kMlaDk + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < kMlaKStepsLat; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * ks);
 #pragma unroll
@@ -558,7 +563,7 @@ mla_attn_kernel(AttnParams p, int workers) {
     const float et = esum + __shfl_xor(esum, 32, 64);
     const int head = kMlaHeadsPerWave * wave + (lane & 31);
     if (whole) {
-      const int64_t row = cur_u * kMlaHeads + head;
+      const int64_t row = cur_u * kMlaHeads + head;  // = ((r * batch + b) * q_len + i) * Hq + head
       float* dst = p.out_o + row * kMlaDv + 4 * h;
       const float inv = 1.f / lt_;
 #pragma unroll
@@ -599,13 +604,13 @@ bool mla_supported(const AttnParams& p) {
   for (int i = 0; i < 4; ++i)
     if ((kv.k_stride[i] * 2) % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(kv.k) % 16) return false;
-  if (static_cast<int64_t>(p.rank_count) * p.batch >= (int64_t(1) << 31)) return false;
+  if (static_cast<int64_t>(p.rank_count) * p.batch * p.q_len >= (int64_t(1) << 31)) return false;
+  if (p.tpu != 1) return false;  // one query token per unit
   return true;
 }
 
 size_t mla_workspace_bytes(const AttnParams& p) {
-  const int64_t U = static_cast<int64_t>(p.rank_count) * p.batch;
-  return split_ws_bytes(U, kMlaMaxWorkers, kMlaHeads, kMlaDv);
+  return split_ws_bytes(split_units_host(p), kMlaMaxWorkers, kMlaHeads, kMlaDv);
 }
 
 hipError_t launch_mla_attn(const AttnParams& p) {

@@ -15,6 +15,11 @@ struct AttnParams {
   const void* q;
   int q_dtype;
   int batch, num_q_heads, group;  // group = num_q_heads / num_kv_heads
+  // Query tokens per request (1: decode; more: the last q_len tokens of each
+  // request at once, query i attending local_lens row (b * q_len + i)). A
+  // split-KV unit covers tpu of them (ntg = ceil(q_len / tpu) units per
+  // request and KV head).
+  int q_len = 1, tpu = 1, ntg = 1;
   dcp_kv_cache_t kv;
   const int32_t* block_table;
   int64_t bt_stride;

@@ -1,8 +1,9 @@
 // Stream-K split of the per-rank partial attention over persistent workers,
 // shared by the GQA and MLA MFMA kernels.
 //
-// A unit is (rank, request, KV head); its local tokens are cut into tiles of
-// `tok` tokens and the tiles of all units, in unit order, are dealt out in
+// A unit is (rank, request, KV head, group of tpu query tokens); its local
+// tokens (as many as its longest query sees) are cut into tiles of `tok`
+// tokens and the tiles of all units, in unit order, are dealt out in
 // equal contiguous ranges (ceil(total / workers) tiles) to the workers. A
 // worker that covers a whole unit writes the unit's final partial (O, LSE)
 // for the rank; a unit cut between workers leaves one unnormalised piece per
@@ -27,7 +28,7 @@ struct SplitWs {
   int64_t* prefix;  // [U + 1] tile prefix over units; prefix[U] = total tiles
   int32_t* wunit;   // [max_workers] unit holding each worker's first tile
   int32_t* todo;    // [1 + U + max_workers]: count, then the units that are empty or cut
-  float* part;      // [max_workers][2][group][Dv + kPartExtra]
+  float* part;      // [max_workers][2][rows][Dv + kPartExtra], rows = tpu * group
 };
 
 __host__ __device__ inline SplitWs split_ws(void* base, int64_t units, int max_workers) {
@@ -43,23 +44,62 @@ __host__ __device__ inline SplitWs split_ws(void* base, int64_t units, int max_w
   return w;
 }
 
-static inline size_t split_ws_bytes(int64_t units, int max_workers, int group, int dv) {
+static inline size_t split_ws_bytes(int64_t units, int max_workers, int rows, int dv) {
   size_t b = align_up(static_cast<size_t>(units + 1) * sizeof(int64_t), 256);
   b += align_up(static_cast<size_t>(max_workers) * sizeof(int32_t), 256);
   b += align_up(static_cast<size_t>(1 + units + max_workers) * sizeof(int32_t), 256);
-  b += static_cast<size_t>(max_workers) * 2 * group * (dv + kPartExtra) * sizeof(float);
+  b += static_cast<size_t>(max_workers) * 2 * rows * (dv + kPartExtra) * sizeof(float);
   return b;
 }
 
-__device__ __forceinline__ int64_t split_units(const AttnParams& p) {
-  return static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads;
+static inline int64_t split_units_host(const AttnParams& p) {
+  return static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads * p.ntg;
 }
 
-// Tiles of unit u = (r * batch + b) * Hkv + h (tok = 1 << tok_log2 tokens each).
+__device__ __forceinline__ int64_t split_units(const AttnParams& p) {
+  return static_cast<int64_t>(p.rank_count) * p.batch * p.kv.num_kv_heads * p.ntg;
+}
+
+// Unit u = ((r * batch + b) * Hkv + h) * ntg + tg covers rank r (counted from
+// rank_begin), request b, KV head h and query tokens [i0, i1) of the request.
+struct UnitRef {
+  int64_t rb;  // r * batch + b
+  int r, b, h, i0, i1;
+};
+
+__device__ __forceinline__ UnitRef unit_ref(const AttnParams& p, int64_t u) {
+  UnitRef x;
+  const int tg = static_cast<int>(u % p.ntg);
+  const int64_t uh = u / p.ntg;
+  x.h = static_cast<int>(uh % p.kv.num_kv_heads);
+  x.rb = uh / p.kv.num_kv_heads;
+  x.b = static_cast<int>(x.rb % p.batch);
+  x.r = static_cast<int>(x.rb / p.batch);
+  x.i0 = tg * p.tpu;
+  x.i1 = min(p.q_len, x.i0 + p.tpu);
+  return x;
+}
+
+// Local tokens query token i of request b sees on rank r (from rank_begin).
+__device__ __forceinline__ int query_len(const AttnParams& p, int b, int i, int r) {
+  return max(p.local_lens[(static_cast<int64_t>(b) * p.q_len + i) * p.dcp_size + p.rank_begin + r], 0);
+}
+
+// Local tokens of a unit: as many as its longest query sees.
+__device__ __forceinline__ int unit_len(const AttnParams& p, const UnitRef& x) {
+  int n = 0;
+  for (int i = x.i0; i < x.i1; ++i) n = max(n, query_len(p, x.b, i, x.r));
+  return n;
+}
+
+// Output row of (query token i, query head h * group + g) of unit x.
+__device__ __forceinline__ int64_t out_row(const AttnParams& p, const UnitRef& x, int i, int g) {
+  return (x.rb * p.q_len + i) * p.num_q_heads + static_cast<int64_t>(x.h) * p.group + g;
+}
+
+// Tiles of unit u (tok = 1 << tok_log2 tokens each).
 __device__ __forceinline__ int64_t unit_tiles(const AttnParams& p, int64_t u, int tok_log2) {
-  const int64_t rb = u / p.kv.num_kv_heads;
-  const int b = static_cast<int>(rb % p.batch), r = static_cast<int>(rb / p.batch);
-  const int64_t n = max(p.local_lens[static_cast<int64_t>(b) * p.dcp_size + p.rank_begin + r], 0);
+  const int64_t n = unit_len(p, unit_ref(p, u));
   return (n + (int64_t(1) << tok_log2) - 1) >> tok_log2;
 }
 
@@ -122,58 +162,65 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
   if (tid == 0) ws.todo[0] = todo_n;
 }
 
-// Fixed grid; one wavefront per (listed unit, query head of its group) item:
-// merge the pieces of a unit cut between workers, or write O = 0 / LSE = -inf
-// for an empty unit.
+// Fixed grid; one wavefront per (listed unit, row of the unit) item, a row
+// being (query token, query head of the group): merge the pieces of a unit
+// cut between workers, or write O = 0 / LSE = -inf for an empty unit and for
+// a row that sees no token of the unit (a query earlier than every local
+// token; its pieces carry m = -inf).
 template <int kDv>
 __global__ void __launch_bounds__(kCombineThreads) split_combine_kernel(AttnParams p, int workers, int max_workers) {
-  const int G = p.group;
+  const int G = p.group, rows = p.tpu * p.group;
   const int64_t U = split_units(p);
   SplitWs ws = split_ws(p.workspace, U, max_workers);
   const int64_t T = ws.prefix[U];
   const int64_t tpw = T > 0 ? (T + workers - 1) / workers : 1;
-  const int64_t items = static_cast<int64_t>(ws.todo[0]) * G;
+  const int64_t items = static_cast<int64_t>(ws.todo[0]) * rows;
   const int lane = threadIdx.x & 63;
   const int64_t wave0 = (static_cast<int64_t>(blockIdx.x) * kCombineThreads + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kCombineThreads) >> 6;
   constexpr int kRow = kDv + kPartExtra;
   constexpr int kPer = (kDv + 63) / 64;
   for (int64_t it = wave0; it < items; it += nwaves) {
-    const int64_t u = ws.todo[1 + it / G];
-    const int g = static_cast<int>(it % G);
-    const int h = static_cast<int>(u % p.kv.num_kv_heads);
-    const int64_t rb = u / p.kv.num_kv_heads;
-    const int64_t row = rb * p.num_q_heads + static_cast<int64_t>(h) * G + g;
+    const int64_t u = ws.todo[1 + it / rows];
+    const int c = static_cast<int>(it % rows);
+    const UnitRef x = unit_ref(p, u);
+    const int i = x.i0 + c / G;
+    if (i >= x.i1) continue;  // a row past the request's last query token
+    const int64_t row = out_row(p, x, i, c % G);
     const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
     float* dst = p.out_o + row * kDv;
-    if (ubeg == uend) {
+    float mx = -INFINITY;
+    int64_t wa = 0, wb = -1;
+    if (ubeg != uend) {
+      wa = ubeg / tpw;
+      wb = (uend - 1) / tpw;
+      for (int64_t w = wa; w <= wb; ++w)
+        mx = fmaxf(mx, ws.part[((w * 2 + (w == wa ? 1 : 0)) * rows + c) * kRow + kDv]);
+    }
+    if (mx == -INFINITY) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i < kDv) dst[lane + 64 * i] = 0.f;
+      for (int k = 0; k < kPer; ++k)
+        if (lane + 64 * k < kDv) dst[lane + 64 * k] = 0.f;
       if (lane == 0) p.out_lse[row] = -INFINITY;
       continue;
     }
-    const int64_t wa = ubeg / tpw, wb = (uend - 1) / tpw;
-    float mx = -INFINITY;
-    for (int64_t w = wa; w <= wb; ++w)
-      mx = fmaxf(mx, ws.part[((w * 2 + (w == wa ? 1 : 0)) * G + g) * kRow + kDv]);
     float acc[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+    for (int k = 0; k < kPer; ++k) acc[k] = 0.f;
     float lsum = 0.f, esum = 0.f;
     for (int64_t w = wa; w <= wb; ++w) {
-      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * G + g) * kRow;
-      const float sc = exp2f(hrow[kDv] - mx);
+      const float* hrow = ws.part + ((w * 2 + (w == wa ? 1 : 0)) * rows + c) * kRow;
+      const float sc = exp2f(hrow[kDv] - mx);  // 0 for a piece with m = -inf
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (lane + 64 * i < kDv) acc[i] += sc * hrow[lane + 64 * i];
+      for (int k = 0; k < kPer; ++k)
+        if (lane + 64 * k < kDv) acc[k] += sc * hrow[lane + 64 * k];
       lsum += sc * hrow[kDv + 1];
       esum += sc * hrow[kDv + 2];
     }
     const float inv = 1.f / lsum;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (lane + 64 * i < kDv) dst[lane + 64 * i] = acc[i] * inv;
+    for (int k = 0; k < kPer; ++k)
+      if (lane + 64 * k < kDv) dst[lane + 64 * k] = acc[k] * inv;
     if (lane == 0) p.out_lse[row] = (mx + __log2f(esum)) * DCP_LN2;
   }
 }

@@ -23,7 +23,7 @@ TORCH_TO_DCP = {torch.float32: DCP_F32, torch.bfloat16: DCP_BF16, torch.float8_e
 EXPORTS = [
     "dcp_abi_version", "dcp_status_string", "dcp_local_seq_lens", "dcp_slot_mapping",
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
-    "dcp_kv_cache_write",
+    "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
     "dcp_profile_enable", "dcp_profile_collect",
 ]
 
@@ -73,6 +73,12 @@ def lib():
                                               i32, i32, f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.dcp_lse_merge.restype = ctypes.c_int
         L.dcp_lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+        L.dcp_partial_verify_attn_workspace_size.restype = ctypes.c_size_t
+        L.dcp_partial_verify_attn_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(KvCache), i32, i32,
+                                                             ctypes.POINTER(ctypes.c_int)]
+        L.dcp_partial_verify_attn.restype = ctypes.c_int
+        L.dcp_partial_verify_attn.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp, i32,
+                                              i32, i32, f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.dcp_kv_cache_write.restype = ctypes.c_int
         L.dcp_kv_cache_write.argtypes = [vp, vp, i32, i64, vp, i32, ctypes.POINTER(KvCache), vp]
         L.dcp_profile_enable.restype = ctypes.c_int
@@ -160,6 +166,33 @@ def dcp_partial_decode_attn(q, kv: KvCache, block_table, local_lens, dcp_size, r
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dcp_partial_decode_attn", lib().dcp_partial_decode_attn(
         _ptr(q), TORCH_TO_DCP[q.dtype], B, Hq, ctypes.byref(kv), _ptr(block_table), block_table.stride(0),
+        max_vblocks, _ptr(local_lens), dcp_size, rank_begin, rank_count, float(softmax_scale), algo,
+        _ptr(out_o), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dcp_partial_verify_attn_workspace_size(batch, q_len, num_q_heads, q_dtype, kv: KvCache, rank_count,
+                                           algo=DCP_ALGO_AUTO) -> int:
+    st = ctypes.c_int(0)
+    n = lib().dcp_partial_verify_attn_workspace_size(batch, q_len, num_q_heads, q_dtype, ctypes.byref(kv),
+                                                    rank_count, algo, ctypes.byref(st))
+    _check("dcp_partial_verify_attn_workspace_size", st.value)
+    return int(n)
+
+
+def dcp_partial_verify_attn(q, kv: KvCache, block_table, local_lens, dcp_size, rank_begin, rank_count,
+                            softmax_scale, out_o, out_lse, workspace, algo=DCP_ALGO_AUTO, max_vblocks=None,
+                            stream=None):
+    """Multi-token decode: ``q [B, q_len, Hq, Dk]``, ``local_lens [B, q_len, dcp_size]`` int32;
+    fills ``out_o [R, B, q_len, Hq, Dv]`` and ``out_lse [R, B, q_len, Hq]`` (float32)."""
+    B, q_len, Hq, _ = q.shape
+    assert q.is_contiguous() and local_lens.dtype == torch.int32 and local_lens.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.stride(1) == 1
+    assert out_o.dtype == torch.float32 and out_lse.dtype == torch.float32
+    if max_vblocks is None:
+        max_vblocks = block_table.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dcp_partial_verify_attn", lib().dcp_partial_verify_attn(
+        _ptr(q), TORCH_TO_DCP[q.dtype], B, q_len, Hq, ctypes.byref(kv), _ptr(block_table), block_table.stride(0),
         max_vblocks, _ptr(local_lens), dcp_size, rank_begin, rank_count, float(softmax_scale), algo,
         _ptr(out_o), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
 

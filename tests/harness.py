@@ -164,3 +164,91 @@ def check_against_oracle(inputs, result, requests=None, check_parts=True, rank_b
             for r in range(R):
                 check_rows(po[r, b], ro[rank_begin + r], tol, f"partial O r={rank_begin + r} b={b}")
                 check_lse(pl[r, b], rl[rank_begin + r], tol, f"partial LSE r={rank_begin + r} b={b}")
+
+
+# ---------------------------------------------------------------------------
+# multi-token decode (speculative verification)
+# ---------------------------------------------------------------------------
+def verify_query_lens(seq_lens, q_len):
+    """[B, q_len] sequence lengths each query token sees: L_b - q_len + i + 1."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    return (lens[:, None] - q_len + np.arange(q_len)[None, :] + 1).astype(np.int32)
+
+
+class VerifyRun:
+    """The HIP path of one multi-token decode step over DeviceInputs' cache:
+    per-query local lengths (dcp_local_seq_lens), every rank's partials
+    (dcp_partial_verify_attn) and the merge over batch * q_len rows."""
+
+    def __init__(self, inputs, q, algo=dcp.DCP_ALGO_AUTO, rank_begin=0, rank_count=None):
+        self.inputs, self.q, self.algo = inputs, q, algo
+        w, dev = inputs.w, q.device
+        B, self.q_len, Hq, _ = q.shape
+        self.rank_begin = rank_begin
+        self.R = R = inputs.D - rank_begin if rank_count is None else rank_count
+        ql = verify_query_lens(inputs.case.seq_lens, self.q_len)
+        assert (ql >= 1).all(), "every queried token must be in the cache"
+        self.local_lens = dcp.dcp_local_seq_lens(torch.from_numpy(ql.reshape(-1)).to(dev), inputs.bs, inputs.D,
+                                                 inputs.I).view(B, self.q_len, inputs.D)
+        self.kv = inputs.cache.descriptor(rank_begin)
+        ws_bytes = dcp.dcp_partial_verify_attn_workspace_size(B, self.q_len, Hq, dcp.native.TORCH_TO_DCP[q.dtype],
+                                                              self.kv, R, algo)
+        self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.po = torch.full((R, B, self.q_len, Hq, w.head_dim_v), float("nan"), dtype=torch.float32, device=dev)
+        self.pl = torch.full((R, B, self.q_len, Hq), float("nan"), dtype=torch.float32, device=dev)
+        od = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.out_format]
+        self.o = torch.full((B * self.q_len, Hq, w.head_dim_v), float("nan"), dtype=od, device=dev)
+        self.lse = torch.full((B * self.q_len, Hq), float("nan"), dtype=torch.float32, device=dev)
+
+    def partial(self):
+        dcp.dcp_partial_verify_attn(self.q, self.kv, self.inputs.block_table, self.local_lens, self.inputs.D,
+                                    self.rank_begin, self.R, self.inputs.w.softmax_scale, self.po, self.pl, self.ws,
+                                    algo=self.algo)
+
+    def merge(self):
+        B, Hq, Dv = self.q.shape[0], self.q.shape[2], self.inputs.w.head_dim_v
+        dcp.dcp_lse_merge(self.po.view(self.R, B * self.q_len, Hq, Dv), self.pl.view(self.R, B * self.q_len, Hq),
+                          sink=self.inputs.sink, out_o=self.o, out_lse=self.lse)
+
+    def step(self):
+        self.partial()
+        self.merge()
+
+    def run(self):
+        self.step()
+        torch.cuda.synchronize()
+        B, Hq, Dv = self.q.shape[0], self.q.shape[2], self.inputs.w.head_dim_v
+        return (self.po, self.pl, self.o.view(B, self.q_len, Hq, Dv), self.lse.view(B, self.q_len, Hq))
+
+
+def oracle_verify_request(case, q, b, dcp_size, interleave):
+    """Float64 oracle for request b's q_len query tokens: causal attention over
+    the cached sequence (with the sink) and the per-rank partials."""
+    w = case.workload
+    qb = ofmt.decode(stored_numpy(q[b]), stored_format(q))                     # [q_len, Hq, Dk]
+    k = ofmt.decode_kv(stored_numpy(case.k[b]), stored_format(case.k[b]), case.k_scale)
+    v = k[:, :, :w.head_dim_v] if case.v is None else ofmt.decode_kv(stored_numpy(case.v[b]),
+                                                                      stored_format(case.v[b]), case.v_scale)
+    full = oatt.verify_attention(qb, k, v, w.softmax_scale, case.sink)
+    own = olay.owners(int(case.seq_lens[b]), w.block_size, dcp_size, interleave)
+    parts = oatt.verify_rank_partials(qb, k, v, w.softmax_scale, own, dcp_size)
+    return full, parts
+
+
+def check_verify_against_oracle(run, result, requests=None, check_parts=True):
+    inputs = run.inputs
+    case, w = inputs.case, inputs.w
+    po, pl, o, lse = [t.float().cpu().numpy() for t in result]
+    tol = TOL[w.kv_format]
+    R = po.shape[0]
+    for b in (range(case.batch) if requests is None else requests):
+        (fo, fl), (ro, rl) = oracle_verify_request(case, run.q.cpu(), b, inputs.D, inputs.I)
+        for i in range(run.q_len):
+            if R == inputs.D:
+                check_rows(o[b, i], fo[i], tol, f"merged O b={b} i={i}", out_bf16=(w.out_format == "bf16"))
+                check_lse(lse[b, i], fl[i], tol, f"merged LSE b={b} i={i}")
+            if check_parts:
+                for r in range(R):
+                    rr = run.rank_begin + r
+                    check_rows(po[r, b, i], ro[rr, i], tol, f"partial O r={rr} b={b} i={i}")
+                    check_lse(pl[r, b, i], rl[rr, i], tol, f"partial LSE r={rr} b={b} i={i}")

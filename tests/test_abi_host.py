@@ -169,3 +169,25 @@ def test_kv_cache_write_validation(L):
     assert call(k=ctypes.c_void_p(p.value + 2)) == UNS         # unaligned source rows
     assert call(T=0, k=NULL, slots=NULL) == 0                  # empty: nothing launched
     assert call(T=0, src=F32, kv=_kv(v=None, head_dim_v=64), v=NULL) == 0
+
+
+def test_verify_validation(L):
+    def ws(q_len, batch=4, hq=8, algo=0, kv=None):
+        st = ctypes.c_int(123)
+        n = L.dcp_partial_verify_attn_workspace_size(batch, q_len, hq, native.DCP_BF16,
+                                                     ctypes.byref(kv if kv is not None else _kv()), 2, algo,
+                                                     ctypes.byref(st))
+        return st.value, n
+    assert ws(0)[0] == INV and ws(65)[0] == INV           # 1 <= q_len <= 64
+    st1, n1 = ws(1)
+    st2, n2 = ws(2)
+    assert st1 == 0 and st2 == 0 and n2 > n1            # two units' rows per worker piece
+    _, n_dec = _ws(L, _kv())
+    assert n1 == n_dec                                   # q_len = 1 is decode
+    assert ws(8, algo=native.DCP_ALGO_GENERIC) == (0, 0)
+    p = _fake(64)
+    f = L.dcp_partial_verify_attn
+    assert f(p, native.DCP_BF16, 4, 0, 8, ctypes.byref(_kv()), p, 4, 4, p, 4, 0, 2, ctypes.c_float(0.1), 0, p, p,
+             p, ctypes.c_size_t(1 << 40), NULL) == INV
+    assert f(p, native.DCP_BF16, 0, 3, 8, ctypes.byref(_kv()), p, 4, 4, p, 4, 0, 2, ctypes.c_float(0.1), 0, p, p,
+             p, ctypes.c_size_t(1 << 40), NULL) == 0     # empty batch: nothing launched

@@ -39,3 +39,21 @@ def test_full_size_sampled(device, name, max_requests):
         reqs = [int(order[0]), int(order[-1])]
     print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
     check_against_oracle(inp, res, requests=reqs)
+
+
+@pytest.mark.parametrize("name", ["gqa_fp8_binned_q2", "gqa_bf16_32k_q4", "mla_bf16_bimodal_q2"])
+def test_verify_full_size_sampled(device, name):
+    """Multi-token decode at the verification workloads' full sizes, in the
+    launch configuration bench.py times; sampled requests against the oracle."""
+    from tests.harness import VerifyRun, check_verify_against_oracle
+    from workloads import get_verify_workload, make_verify_queries
+    vw = get_verify_workload(name)
+    w = vw.geometry()
+    case = make_case(w, device=device)
+    inp = DeviceInputs(case, device, fill="zero")
+    run = VerifyRun(inp, make_verify_queries(w, case.batch, vw.q_len, device), algo=dcp.DCP_ALGO_AUTO)
+    res = run.run()
+    assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
+    reqs = _sample(case.seq_lens, w.seed + 1)[:3]
+    print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
+    check_verify_against_oracle(run, res, requests=reqs)

@@ -1,4 +1,5 @@
-"""The five synthetic decode workloads and the two KV-cache write workloads,
+"""The five synthetic decode workloads, the multi-token decode (speculative
+verification) workloads built on them, and the KV-cache write workloads,
 named by what they are.
 
 Length laws ("k" = 1024 tokens):
@@ -153,3 +154,36 @@ def get_kv_write_workload(name: str) -> KvWriteWorkload:
     if name not in KV_WRITE_WORKLOADS:
         raise KeyError(f"unknown KV-write workload {name!r}; known: {sorted(KV_WRITE_WORKLOADS)}")
     return KV_WRITE_WORKLOADS[name]
+
+
+@dataclass(frozen=True)
+class VerifyWorkload:
+    """Multi-token decode on a decode workload's batch: the last ``q_len``
+    tokens of every request are queried at once, causal among them (MTP /
+    speculative verification of q_len - 1 draft tokens)."""
+    name: str
+    base: str
+    q_len: int
+    description: str = ""
+
+    def geometry(self) -> Workload:
+        return WORKLOADS[self.base]
+
+
+VERIFY_WORKLOADS = {
+    w.name: w
+    for w in [
+        VerifyWorkload(name="gqa_fp8_binned_q2", base="gqa_fp8_binned", q_len=2,
+                       description="gqa_fp8_binned batch, 2 query tokens per request (one draft token)"),
+        VerifyWorkload(name="gqa_bf16_32k_q4", base="gqa_bf16_32k", q_len=4,
+                       description="gqa_bf16_32k batch, 4 query tokens per request (three draft tokens)"),
+        VerifyWorkload(name="mla_bf16_bimodal_q2", base="mla_bf16_bimodal", q_len=2,
+                       description="mla_bf16_bimodal batch, 2 query tokens per request (one draft token)"),
+    ]
+}
+
+
+def get_verify_workload(name: str) -> VerifyWorkload:
+    if name not in VERIFY_WORKLOADS:
+        raise KeyError(f"unknown verify workload {name!r}; known: {sorted(VERIFY_WORKLOADS)}")
+    return VERIFY_WORKLOADS[name]

@@ -2,7 +2,8 @@
 
 Streams: ``numpy.random.SeedSequence(entropy=seed, spawn_key=(stream, i))``
 with stream 0 = lengths, 1 = block permutation, 2 = q, 3 = K, 4 = V,
-5 = fp8 scales and sinks, 6 = needles. K and V are drawn per request, in
+5 = fp8 scales and sinks, 6 = needles, 7 = KV-write contexts, 8 = the
+queries of multi-token decode. K and V are drawn per request, in
 canonical (request-contiguous) token order, with a torch generator on the
 requested device, so large batches are produced in device memory; the stored
 values are what both the oracle (after a copy to the host) and the GPU path
@@ -29,7 +30,7 @@ import torch
 
 from .configs import KvWriteWorkload, Workload
 
-LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES, CONTEXT = range(8)
+LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES, CONTEXT, VERIFYQ = range(9)
 
 TORCH_FORMAT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
 
@@ -216,3 +217,10 @@ def make_kv_write_case(w: KvWriteWorkload, device="cpu") -> KvWriteCase:
     k_scale = _scales(g, 0) if fp8 else None
     v_scale = _scales(g, 1) if fp8 and not g.mla else None
     return KvWriteCase(w, ctx, positions, reqs, table, num_blocks, k_new, v_new, k_scale, v_scale)
+
+
+def make_verify_queries(w: Workload, batch: int, q_len: int, device="cpu") -> torch.Tensor:
+    """Seeded queries ``[batch, q_len, Hq, Dk]`` ~ N(0, 1) in ``q_format`` for
+    multi-token decode of the last ``q_len`` tokens of each request."""
+    q32 = _randn((batch, q_len, w.num_q_heads, w.head_dim_k), _seed(w.seed, VERIFYQ, q_len), device)
+    return q32.to(TORCH_FORMAT[w.q_format])
