@@ -15,7 +15,9 @@ Sources:
 * "DeepSeek V4.1 context parallelism", section "Decode computation": the
   attention sink is applied once, when the partial outputs are merged by
   log-sum-exp; decode and speculative (DSpark) verification share the decode
-  path, each rank attending the pages it owns.
+  path, each rank attending the pages it owns; a replicated segment (the
+  sliding-window cache, section "Cache ownership": kept on every rank)
+  contributes on one rank only.
 * "Efficient Decode Context Parallelism with vLLM for Long Context Workloads",
   section 6 (MTP and speculative decoding on the DCP decode path).
 
@@ -32,7 +34,11 @@ the pages are silent:
   row (latent part), so the caller passes ``v = k[..., :Dv]``;
 * multi-token decode: the ``q_len`` queried tokens are the last ``q_len``
   positions, already in the cache, and query ``i`` attends every position up
-  to its own (``verify_attention``).
+  to its own (``verify_attention``);
+* a replicated segment is a separate set of KV entries that joins the
+  attention of every query of its request (the reference is plain attention
+  over the sharded sequence and the segment together); one designated rank
+  adds it to its partial (``segment_rank_partials``).
 """
 
 import numpy as np
@@ -121,6 +127,23 @@ def verify_rank_partials(q, k, v, scale: float, owner, dcp_size: int):
         os_.append(o)
         ls_.append(lse)
     return np.stack(os_, axis=1), np.stack(ls_, axis=1)
+
+
+def segment_rank_partials(q, k, v, scale: float, owner, dcp_size: int, k_seg, v_seg, seg_rank: int):
+    """Per-rank partials when a replicated segment (its own tokens ``k_seg``,
+    ``v_seg``, e.g. a sliding-window cache kept on every rank) joins the
+    attention: rank ``seg_rank`` attends its owned tokens and the segment,
+    every other rank only its owned tokens, so the merge counts the segment
+    once. Returns ``(O [D, Hq, Dv], LSE [D, Hq])``."""
+    owner = np.asarray(owner)
+    out = []
+    for r in range(dcp_size):
+        kr, vr = k[owner == r], v[owner == r]
+        if r == seg_rank:
+            kr = np.concatenate([kr, k_seg], axis=0)
+            vr = np.concatenate([vr, v_seg], axis=0)
+        out.append(decode_attention(q, kr, vr, scale))
+    return np.stack([o for o, _ in out]), np.stack([l for _, l in out])
 
 
 def lse_merge(part_o, part_lse, sink=None):
