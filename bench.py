@@ -22,6 +22,11 @@ rank's partial attention for the last N tokens of every request at once
 (causal among them) plus the merge; ``value`` counts the KV bytes of the
 batch once, like decode, and ``config`` adds the verified tokens per second.
 
+With a replicated-segment workload (``--workload *_swa<W>``) a step is every
+rank's partial attention, the fold of each request's W-token segment into
+the designated rank's partial, and the merge (sink once); ``value`` counts
+the sharded KV and the segments once.
+
 With ``--workload kvw_*`` a step is instead the KV-cache write of a batch of
 new tokens (slot mapping, then the write of every row into its owner's pool);
 ``value`` and ``roofline`` then count the write's algorithmic bytes (new rows
@@ -45,6 +50,7 @@ METRIC = "decode-attn KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU
 DEFAULT_WORKLOAD = "gqa_fp8_binned"
 KV_WRITE_METRIC = "KV-cache write GB/s (new rows + slots read, stored rows written) at 1 GPU"
 VERIFY_METRIC = "multi-token decode KV GB/s (% of MI355X HBM peak) + verified tokens/s at 1 GPU"
+SEGMENT_METRIC = "decode with a replicated segment: KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU"
 KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
                 "kv_write": "kv_write"}
 KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip",
@@ -390,6 +396,137 @@ def bench_verify(args, vw):
     print(json.dumps(out), flush=True)
 
 
+def bench_segment(args, sw):
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from tests.harness import DeviceInputs, SegmentInputs
+    from workloads import make_case, make_segment
+
+    w = sw.geometry()
+    t_gen = time.perf_counter()
+    case = make_case(w, device="cuda")
+    inp = DeviceInputs(case, "cuda", fill="zero")
+    seg = make_segment(w, case.seq_lens, sw.window, case.k_scale, case.v_scale, "cuda")
+    sgi = SegmentInputs(inp, seg, "cuda")
+    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    seg_bytes = int(seg.lens.astype(np.int64).sum()) * w.kv_bytes_per_token()
+    kv_bytes = case.kv_bytes() + seg_bytes
+    print(f"[bench] {sw.name}: batch {case.batch}, {int(case.seq_lens.sum())} sharded + {int(seg.lens.sum())} "
+          f"segment tokens, {kv_bytes / 1e9:.3f} GB KV, inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def step():
+        inp.partial()
+        sgi.fold(sw.seg_rank)
+        inp.merge()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dcp.native.dcp_profile_enable(True)
+    dcp.native.dcp_profile_collect()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern_ms, launches = dcp.native.dcp_profile_collect()
+    dcp.native.dcp_profile_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    kern_avg_ms = kern_ms / max(launches, 1)
+    # the segment call alone (its attention over the segments and the fold)
+    start.record()
+    for _ in range(args.steps):
+        sgi.fold(sw.seg_rank)
+    stop.record()
+    torch.cuda.synchronize()
+    seg_ms = start.elapsed_time(stop) / args.steps
+    family = kernel_family(w)
+    out = {
+        "metric": SEGMENT_METRIC,
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": sw.name,
+            "base": w.name,
+            "window": sw.window,
+            "seg_rank": sw.seg_rank,
+            "batch": case.batch,
+            "kv_format": w.kv_format,
+            "dcp_size": w.dcp_size,
+            "interleave": w.interleave,
+            "tokens": int(case.seq_lens.astype(np.int64).sum()),
+            "segment_tokens": int(seg.lens.astype(np.int64).sum()),
+            "kv_bytes": int(kv_bytes),
+            "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "merged_queries_per_s": round(case.batch / (ms * 1e-3), 1),
+            "segment_call_ms": round(seg_ms, 5),
+            "kernel": KERNEL_NAMES[family],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(case.kv_bytes() / (kern_avg_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(case.kv_bytes() / (kern_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_avg_ms": round(kern_avg_ms, 5),
+            "note": "the sharded attention kernel (the segment call is timed separately in config)",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_segment(case, seg, sw, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_segment(case, seg, sw, budget_s):
+    """Time the float64 oracle (attention over each request's sequence and segment) on a sample."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import formats as ofmt
+    from workloads.generate import stored_format, stored_numpy
+    w = case.workload
+    order = np.random.default_rng(12345).permutation(case.batch)
+    spent, kv_bytes, done = 0.0, 0, []
+    for b in order:
+        q_st = stored_numpy(case.q[b])
+        arrs = [(stored_numpy(t), stored_format(t)) for t in (case.k[b], seg.k[b])]
+        varrs = None if case.v is None else [(stored_numpy(t), stored_format(t)) for t in (case.v[b], seg.v[b])]
+        t0 = time.perf_counter()
+        q = ofmt.decode(q_st, stored_format(case.q))
+        k = np.concatenate([ofmt.decode_kv(a, f, case.k_scale) for a, f in arrs])
+        v = k[:, :, :w.head_dim_v] if varrs is None else np.concatenate(
+            [ofmt.decode_kv(a, f, case.v_scale) for a, f in varrs])
+        oatt.decode_attention(q, k, v, w.softmax_scale, case.sink)
+        spent += time.perf_counter() - t0
+        kv_bytes += (int(case.seq_lens[b]) + int(seg.lens[b])) * w.kv_bytes_per_token()
+        done.append(int(b))
+        if spent >= budget_s:
+            break
+    return {
+        "value": kv_bytes / spent / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads()),
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {case.batch} requests (seeded random order), full softmax over the sequence "
+                   f"and its {sw.window}-token segment in float64 incl. decoding the stored KV; {spent:.1f} s"),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,9 +571,12 @@ def main():
     if args.workload.startswith("kvw_"):
         bench_kv_write(args, args.workload)
         return
-    from workloads import VERIFY_WORKLOADS
+    from workloads import SEGMENT_WORKLOADS, VERIFY_WORKLOADS
     if args.workload in VERIFY_WORKLOADS:
         bench_verify(args, VERIFY_WORKLOADS[args.workload])
+        return
+    if args.workload in SEGMENT_WORKLOADS:
+        bench_segment(args, SEGMENT_WORKLOADS[args.workload])
         return
     w = get_workload(args.workload)
     t_gen = time.perf_counter()

@@ -253,6 +253,55 @@ int dcp_partial_verify_attn(const void* q, int32_t q_dtype, int32_t batch, int32
                             size_t workspace_bytes, void* stream);
 
 /*
+ * dcp_partial_segment_attn - add a replicated segment to the one rank that
+ * counts it.
+ *
+ * Source: "DeepSeek V4.1 context parallelism", sections "Cache ownership"
+ * (the sliding-window (SWA) cache stays replicated on every rank) and
+ * "Decode computation" (replicated SWA contributes on one rank; the sink is
+ * applied once in the log-sum-exp merge).
+ *
+ * A segment is a set of KV entries per request kept whole on every rank
+ * (e.g. the SWA window), separate from the sharded cache; every query head of
+ * the request attends it in addition to the sharded tokens. This call
+ * computes each request's attention over its segment (seg_lens[b] tokens of
+ * the paged pool seg_kv, read through seg_block_table as a one-rank cache:
+ * token j in block seg_block_table[b * stride + j / block_size], slot
+ * j % block_size of pool 0) and folds it in place into the partial of rank
+ * seg_rank:
+ *   LSE' = ln(exp(LSE_r) + exp(LSE_seg)),
+ *   O'   = exp(LSE_r - LSE') O_r + exp(LSE_seg - LSE') O_seg
+ * (an empty side contributes nothing; both empty leaves O = 0, LSE = -inf).
+ * Every other rank's partial is left as it is, so dcp_lse_merge afterwards
+ * counts the segment exactly once (and the sink once). Call it after
+ * dcp_partial_decode_attn and before dcp_lse_merge.
+ *
+ * q, q_dtype, batch, num_q_heads, softmax_scale, algo: as for
+ *             dcp_partial_decode_attn (one query token per request)
+ * seg_kv      the segment pool (rank index 0; num_kv_heads and head dims as
+ *             the sharded cache; MLA: v == NULL)
+ * seg_lens    device, [batch] int32, each <= seg_max_vblocks * block_size
+ * seg_rank    the rank that counts the segment, >= 0; when it lies outside
+ *             [rank_begin, rank_begin + rank_count) nothing is launched (the
+ *             GPU holding that rank adds it)
+ * part_o, part_lse  device, the partials dcp_partial_decode_attn wrote for
+ *             ranks rank_begin .. rank_begin + rank_count - 1; updated in place
+ * workspace   device, >= dcp_partial_segment_attn_workspace_size bytes
+ * Errors: as for dcp_partial_decode_attn.
+ */
+size_t dcp_partial_segment_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
+                                               const dcp_kv_cache_t* seg_kv, int32_t algo,
+                                               int* status);
+
+int dcp_partial_segment_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                             const dcp_kv_cache_t* seg_kv, const int32_t* seg_block_table,
+                             int64_t seg_block_table_stride, int32_t seg_max_vblocks,
+                             const int32_t* seg_lens, float softmax_scale, int32_t algo,
+                             int32_t seg_rank, int32_t rank_begin, int32_t rank_count,
+                             float* part_o, float* part_lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * dcp_lse_merge - combine per-rank partials into exact attention, applying an
  * attention sink once.
  *

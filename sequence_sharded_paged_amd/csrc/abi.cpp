@@ -194,7 +194,7 @@ static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q
                         const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
                         int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
                         int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream, bool profiled = true) {
   AttnParams p{};
   AttnKernel k = AttnKernel::Generic;
   if (int st = validate_attn(batch, q_len, num_q_heads, q_dtype, kv, rank_count, algo, p, k)) return st;
@@ -219,7 +219,7 @@ static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q
   p.workspace = workspace;
   p.workspace_bytes = workspace_bytes;
   p.stream = static_cast<hipStream_t>(stream);
-  const auto ev = profile_next();
+  const auto ev = profiled ? profile_next() : std::pair<hipEvent_t, hipEvent_t>{nullptr, nullptr};
   p.ev_begin = ev.first;
   p.ev_end = ev.second;
   hipError_t e;
@@ -231,9 +231,64 @@ static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q
   return e == hipSuccess ? DCP_OK : DCP_ERR_HIP;
 }
 
+// Workspace of dcp_partial_segment_attn: the segment's partial O [B, Hq, Dv]
+// and LSE [B, Hq], then the attention workspace for the segment pool.
+struct SegmentWs {
+  size_t o_bytes, lse_bytes, attn_bytes;
+  size_t total() const { return o_bytes + lse_bytes + attn_bytes; }
+};
+
+static int segment_ws(int32_t batch, int32_t num_q_heads, int32_t q_dtype, const dcp_kv_cache_t* seg_kv,
+                      int32_t algo, SegmentWs& w) {
+  int st = DCP_OK;
+  w.attn_bytes = attn_workspace_size(batch, 1, num_q_heads, q_dtype, seg_kv, 1, algo, &st);
+  if (st != DCP_OK) return st;
+  w.o_bytes = align_up(static_cast<size_t>(batch) * num_q_heads * seg_kv->head_dim_v * sizeof(float), 256);
+  w.lse_bytes = align_up(static_cast<size_t>(batch) * num_q_heads * sizeof(float), 256);
+  return DCP_OK;
+}
+
 }  // namespace dcp
 
 extern "C" {
+
+size_t dcp_partial_segment_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
+                                               const dcp_kv_cache_t* seg_kv, int32_t algo, int* status) {
+  SegmentWs w{};
+  const int st = segment_ws(batch, num_q_heads, q_dtype, seg_kv, algo, w);
+  if (status) *status = st;
+  return st == DCP_OK ? w.total() : 0;
+}
+
+int dcp_partial_segment_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                             const dcp_kv_cache_t* seg_kv, const int32_t* seg_block_table,
+                             int64_t seg_block_table_stride, int32_t seg_max_vblocks, const int32_t* seg_lens,
+                             float softmax_scale, int32_t algo, int32_t seg_rank, int32_t rank_begin,
+                             int32_t rank_count, float* part_o, float* part_lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  SegmentWs w{};
+  if (int st = segment_ws(batch, num_q_heads, q_dtype, seg_kv, algo, w)) return st;
+  if (rank_begin < 0 || rank_count < 1 || seg_rank < 0) return DCP_ERR_INVALID_ARG;
+  if (seg_rank < rank_begin || seg_rank >= rank_begin + rank_count) return DCP_OK;  // another GPU's rank counts it
+  if (batch == 0) return DCP_OK;
+  if (!part_o || !part_lse) return DCP_ERR_INVALID_ARG;
+  if (workspace_bytes < w.total() || !workspace) return DCP_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* o_seg = reinterpret_cast<float*>(ws);
+  float* lse_seg = reinterpret_cast<float*>(ws + w.o_bytes);
+  void* attn_ws = ws + w.o_bytes + w.lse_bytes;
+  // the segment as a one-rank pool: its lengths are its local lengths
+  if (int st = partial_attn(q, q_dtype, batch, 1, num_q_heads, seg_kv, seg_block_table, seg_block_table_stride,
+                            seg_max_vblocks, seg_lens, 1, 0, 1, softmax_scale, algo, o_seg, lse_seg, attn_ws,
+                            w.attn_bytes, stream, false))
+    return st;
+  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
+  const int64_t r = seg_rank - rank_begin;
+  return launch_lse_fold(part_o + r * rows * seg_kv->head_dim_v, part_lse + r * rows, o_seg, lse_seg, rows,
+                         seg_kv->head_dim_v, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DCP_OK
+             : DCP_ERR_HIP;
+}
 
 size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t q_dtype,
                                               const dcp_kv_cache_t* kv, int32_t rank_count, int32_t algo,

@@ -61,6 +61,8 @@ hipError_t launch_slot_mapping(const int64_t* positions, const int32_t* req_indi
                                int interleave, int64_t* slots, hipStream_t s);
 hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_bf16, int64_t num_tokens,
                            const int64_t* slots, int num_ranks, const dcp_kv_cache_t& kv, hipStream_t stream);
+hipError_t launch_lse_fold(float* o, float* lse, const float* o_add, const float* lse_add, int64_t rows,
+                           int head_dim_v, hipStream_t s);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, int num_parts, int batch,
                             int num_heads, int head_dim_v, const float* sink, int out_dtype,
                             void* out_o, float* out_lse, hipStream_t s);

@@ -10,7 +10,8 @@
 // One workgroup per (request, head); every thread derives the merge weights
 // from the num_parts LSE values (read once into LDS) and then scales and sums
 // its slice of the head's output rows. HBM bound: reads num_parts*(Dv+1)
-// floats and writes Dv outputs per (request, head).
+// floats and writes Dv outputs per (request, head). The same file holds the
+// in-place fold that adds a replicated segment's partial to one rank's.
 #include "common.h"
 
 namespace dcp {
@@ -56,6 +57,49 @@ __global__ void __launch_bounds__(kMergeThreads) lse_merge_kernel(
     if (kBf16Out) reinterpret_cast<uint16_t*>(out_o)[o] = f32_to_bf16_bits(acc);
     else reinterpret_cast<float*>(out_o)[o] = acc;
   }
+}
+
+// In-place fold of a second partial into a first: (O, LSE) of attention over
+// the union of two disjoint token sets from the two sets' partials. Used to
+// add a replicated segment to the one rank that counts it. One workgroup per
+// (request, head); wave 0 reads the two LSE values and shares the weights.
+__global__ void __launch_bounds__(kMergeThreads) lse_fold_kernel(float* __restrict__ o, float* __restrict__ lse,
+                                                                 const float* __restrict__ o_add,
+                                                                 const float* __restrict__ lse_add, int head_dim_v) {
+  __shared__ float wts[2];
+  const int64_t bh = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const float l1 = lse[bh], l2 = lse_add[bh];
+    const float m = fmaxf(l1, l2);
+    if (m == -INFINITY) {  // both empty: O stays 0, LSE -inf
+      wts[0] = 1.f;
+      wts[1] = 0.f;
+    } else {
+      const float e1 = l1 == -INFINITY ? 0.f : __expf(l1 - m);
+      const float e2 = l2 == -INFINITY ? 0.f : __expf(l2 - m);
+      const float z = e1 + e2;
+      wts[0] = e1 / z;
+      wts[1] = e2 / z;
+      lse[bh] = m + __logf(z);
+    }
+  }
+  __syncthreads();
+  const float w1 = wts[0], w2 = wts[1];
+  float* dst = o + bh * head_dim_v;
+  const float* add = o_add + bh * head_dim_v;
+  for (int d = threadIdx.x; d < head_dim_v; d += kMergeThreads) {
+    float acc = w1 != 0.f ? w1 * dst[d] : 0.f;
+    if (w2 != 0.f) acc += w2 * add[d];
+    dst[d] = acc;
+  }
+}
+
+hipError_t launch_lse_fold(float* o, float* lse, const float* o_add, const float* lse_add, int64_t rows,
+                           int head_dim_v, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_fold_kernel, dim3(static_cast<unsigned>(rows)), dim3(kMergeThreads), 0, s, o, lse, o_add,
+                     lse_add, head_dim_v);
+  return hipGetLastError();
 }
 
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, int num_parts, int batch,

@@ -24,6 +24,7 @@ EXPORTS = [
     "dcp_abi_version", "dcp_status_string", "dcp_local_seq_lens", "dcp_slot_mapping",
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
     "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
+    "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn",
     "dcp_profile_enable", "dcp_profile_collect",
 ]
 
@@ -79,6 +80,12 @@ def lib():
         L.dcp_partial_verify_attn.restype = ctypes.c_int
         L.dcp_partial_verify_attn.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp, i32,
                                               i32, i32, f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dcp_partial_segment_attn_workspace_size.restype = ctypes.c_size_t
+        L.dcp_partial_segment_attn_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(KvCache), i32,
+                                                              ctypes.POINTER(ctypes.c_int)]
+        L.dcp_partial_segment_attn.restype = ctypes.c_int
+        L.dcp_partial_segment_attn.argtypes = [vp, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp, f32, i32,
+                                               i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.dcp_kv_cache_write.restype = ctypes.c_int
         L.dcp_kv_cache_write.argtypes = [vp, vp, i32, i64, vp, i32, ctypes.POINTER(KvCache), vp]
         L.dcp_profile_enable.restype = ctypes.c_int
@@ -195,6 +202,33 @@ def dcp_partial_verify_attn(q, kv: KvCache, block_table, local_lens, dcp_size, r
         _ptr(q), TORCH_TO_DCP[q.dtype], B, q_len, Hq, ctypes.byref(kv), _ptr(block_table), block_table.stride(0),
         max_vblocks, _ptr(local_lens), dcp_size, rank_begin, rank_count, float(softmax_scale), algo,
         _ptr(out_o), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dcp_partial_segment_attn_workspace_size(batch, num_q_heads, q_dtype, seg_kv: KvCache,
+                                            algo=DCP_ALGO_AUTO) -> int:
+    st = ctypes.c_int(0)
+    n = lib().dcp_partial_segment_attn_workspace_size(batch, num_q_heads, q_dtype, ctypes.byref(seg_kv), algo,
+                                                     ctypes.byref(st))
+    _check("dcp_partial_segment_attn_workspace_size", st.value)
+    return int(n)
+
+
+def dcp_partial_segment_attn(q, seg_kv: KvCache, seg_block_table, seg_lens, softmax_scale, seg_rank, rank_begin,
+                             rank_count, part_o, part_lse, workspace, algo=DCP_ALGO_AUTO, seg_max_vblocks=None,
+                             stream=None):
+    """Fold each request's attention over its replicated segment into rank
+    ``seg_rank``'s partial (``part_o [R, B, Hq, Dv]``, ``part_lse [R, B, Hq]``, in place)."""
+    B, Hq, _ = q.shape
+    assert q.is_contiguous() and seg_lens.dtype == torch.int32 and seg_lens.is_contiguous()
+    assert seg_block_table.dtype == torch.int32 and seg_block_table.stride(1) == 1
+    assert part_o.dtype == torch.float32 and part_lse.dtype == torch.float32
+    if seg_max_vblocks is None:
+        seg_max_vblocks = seg_block_table.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dcp_partial_segment_attn", lib().dcp_partial_segment_attn(
+        _ptr(q), TORCH_TO_DCP[q.dtype], B, Hq, ctypes.byref(seg_kv), _ptr(seg_block_table),
+        seg_block_table.stride(0), seg_max_vblocks, _ptr(seg_lens), float(softmax_scale), algo, seg_rank,
+        rank_begin, rank_count, _ptr(part_o), _ptr(part_lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dcp_lse_merge(part_o, part_lse, sink=None, out_dtype=torch.float32, out_o=None, out_lse=None,

@@ -252,3 +252,76 @@ def check_verify_against_oracle(run, result, requests=None, check_parts=True):
                     rr = run.rank_begin + r
                     check_rows(po[r, b, i], ro[rr, i], tol, f"partial O r={rr} b={b} i={i}")
                     check_lse(pl[r, b, i], rl[rr, i], tol, f"partial LSE r={rr} b={b} i={i}")
+
+
+# ---------------------------------------------------------------------------
+# replicated segment (a sliding-window cache counted by one rank)
+# ---------------------------------------------------------------------------
+class SegmentInputs:
+    """A generated Segment in device memory: a one-rank pool of the cache's
+    geometry (NaN-filled), its block table and lengths, and the call that
+    folds it into one rank's partial."""
+
+    def __init__(self, inputs, seg, device="cuda"):
+        w = inputs.w
+        self.inputs, self.seg = inputs, seg
+        self.lens = torch.from_numpy(seg.lens).to(device)
+        self.block_table = torch.from_numpy(seg.block_table).to(device)
+        self.cache = dcp.PagedKVCache(1, seg.num_blocks, w.block_size, w.num_kv_heads, w.head_dim_k, w.head_dim_v,
+                                      inputs.cache.dtype, mla=w.mla, device=device,
+                                      k_scale=inputs.case.k_scale, v_scale=inputs.case.v_scale, fill="nan")
+        for b in range(len(seg.lens)):
+            L = int(seg.lens[b])
+            if L == 0:
+                continue
+            pos = torch.arange(L, dtype=torch.int64, device=device)
+            req = torch.full((L,), b, dtype=torch.int32, device=device)
+            slots = dcp.dcp_slot_mapping(pos, req, self.block_table, w.block_size, 1, 1)
+            self.cache.write(slots, seg.k[b].to(device), None if seg.v is None else seg.v[b].to(device))
+        self.kv = self.cache.descriptor(0)
+        B, Hq = inputs.q.shape[0], inputs.q.shape[1]
+        n = dcp.dcp_partial_segment_attn_workspace_size(B, Hq, dcp.native.TORCH_TO_DCP[inputs.q.dtype], self.kv)
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+
+    def fold(self, seg_rank, algo=dcp.DCP_ALGO_AUTO):
+        i = self.inputs
+        dcp.dcp_partial_segment_attn(i.q, self.kv, self.block_table, self.lens, i.w.softmax_scale, seg_rank,
+                                     i.rank_begin, i.rank_count, i.po, i.pl, self.ws, algo=algo)
+
+
+def oracle_segment_request(case, seg, b, dcp_size, interleave, seg_rank):
+    """Float64 oracle for request b with its segment: attention over the
+    sequence and the segment together (sink included) and the per-rank
+    partials with the segment on rank seg_rank."""
+    w = case.workload
+    q = ofmt.decode(stored_numpy(case.q[b]), stored_format(case.q))
+
+    def kv(kt, vt):
+        k = ofmt.decode_kv(stored_numpy(kt), stored_format(kt), case.k_scale)
+        v = k[:, :, :w.head_dim_v] if vt is None else ofmt.decode_kv(stored_numpy(vt), stored_format(vt),
+                                                                      case.v_scale)
+        return k, v
+
+    k, v = kv(case.k[b], None if case.v is None else case.v[b])
+    ks, vs = kv(seg.k[b], None if seg.v is None else seg.v[b])
+    full = oatt.decode_attention(q, np.concatenate([k, ks]), np.concatenate([v, vs]), w.softmax_scale, case.sink)
+    own = olay.owners(int(case.seq_lens[b]), w.block_size, dcp_size, interleave)
+    parts = oatt.segment_rank_partials(q, k, v, w.softmax_scale, own, dcp_size, ks, vs, seg_rank)
+    return full, parts
+
+
+def check_segment_against_oracle(inputs, seg, seg_rank, result, requests=None):
+    case, w = inputs.case, inputs.w
+    po, pl, o, lse = [t.float().cpu().numpy() for t in result]
+    tol = TOL[w.kv_format]
+    R = po.shape[0]
+    for b in (range(case.batch) if requests is None else requests):
+        (fo, fl), (ro, rl) = oracle_segment_request(case, seg, b, inputs.D, inputs.I, seg_rank)
+        if R == inputs.D:
+            check_rows(o[b], fo, tol, f"merged O b={b}", out_bf16=(w.out_format == "bf16"))
+            check_lse(lse[b], fl, tol, f"merged LSE b={b}")
+        for r in range(R):
+            rr = inputs.rank_begin + r
+            check_rows(po[r, b], ro[rr], tol, f"partial O r={rr} b={b}")
+            check_lse(pl[r, b], rl[rr], tol, f"partial LSE r={rr} b={b}")

@@ -191,3 +191,22 @@ def test_verify_validation(L):
              p, ctypes.c_size_t(1 << 40), NULL) == INV
     assert f(p, native.DCP_BF16, 0, 3, 8, ctypes.byref(_kv()), p, 4, 4, p, 4, 0, 2, ctypes.c_float(0.1), 0, p, p,
              p, ctypes.c_size_t(1 << 40), NULL) == 0     # empty batch: nothing launched
+
+
+def test_segment_validation(L):
+    st = ctypes.c_int(5)
+    n = L.dcp_partial_segment_attn_workspace_size(4, 8, native.DCP_BF16, ctypes.byref(_kv()), 0, ctypes.byref(st))
+    assert st.value == 0 and n > 4 * 8 * 128 * 4           # segment partial + attention workspace
+    p = _fake(64)
+    f = L.dcp_partial_segment_attn
+
+    def call(seg_rank=1, rb=0, rc=2, part=p, ws_bytes=1 << 40, batch=4):
+        return f(p, native.DCP_BF16, batch, 8, ctypes.byref(_kv()), p, 4, 4, p, ctypes.c_float(0.1), 0, seg_rank,
+                 rb, rc, part, p, p, ctypes.c_size_t(ws_bytes), NULL)
+
+    assert call(seg_rank=-1) == INV
+    assert call(rc=0) == INV
+    assert call(seg_rank=5) == 0          # another GPU's rank counts the segment: nothing launched
+    assert call(part=NULL) == INV
+    assert call(ws_bytes=16) == WS
+    assert call(batch=0) == 0

@@ -57,3 +57,27 @@ def test_verify_full_size_sampled(device, name):
     reqs = _sample(case.seq_lens, w.seed + 1)[:3]
     print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
     check_verify_against_oracle(run, res, requests=reqs)
+
+
+@pytest.mark.parametrize("name", ["mla_bf16_longtail_sink_swa128", "gqa_fp8_binned_swa128"])
+def test_segment_full_size_sampled(device, name):
+    """Decode with a replicated segment at full size, in bench.py's launch
+    configuration; sampled requests against the oracle."""
+    from tests.harness import SegmentInputs, check_segment_against_oracle
+    from workloads import get_segment_workload, make_segment
+    sw = get_segment_workload(name)
+    w = sw.geometry()
+    case = make_case(w, device=device)
+    inp = DeviceInputs(case, device, fill="zero")
+    seg = make_segment(w, case.seq_lens, sw.window, case.k_scale, case.v_scale, device)
+    sgi = SegmentInputs(inp, seg, device)
+    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
+    inp.partial()
+    sgi.fold(sw.seg_rank)
+    inp.merge()
+    torch.cuda.synchronize()
+    res = (inp.po, inp.pl, inp.o, inp.lse)
+    assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
+    reqs = _sample(case.seq_lens, w.seed + 2)[:2]
+    print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
+    check_segment_against_oracle(inp, seg, sw.seg_rank, res, requests=reqs)

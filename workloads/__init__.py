@@ -13,6 +13,8 @@ with a tail to ~1M, ~18% under 8k, ~8% over 128k). None of that trace's items
 are used; only its length statistics shape the mixtures below.
 """
 
-from .configs import (KV_WRITE_WORKLOADS, VERIFY_WORKLOADS, WORKLOADS, KvWriteWorkload,  # noqa: F401
-                      VerifyWorkload, Workload, get_kv_write_workload, get_verify_workload, get_workload)
-from .generate import Case, KvWriteCase, make_case, make_kv_write_case, make_verify_queries  # noqa: F401
+from .configs import (KV_WRITE_WORKLOADS, SEGMENT_WORKLOADS, VERIFY_WORKLOADS, WORKLOADS,  # noqa: F401
+                      KvWriteWorkload, SegmentWorkload, VerifyWorkload, Workload, get_kv_write_workload,
+                      get_segment_workload, get_verify_workload, get_workload)
+from .generate import (Case, KvWriteCase, Segment, make_case, make_kv_write_case, make_segment,  # noqa: F401
+                       make_verify_queries)

@@ -1,6 +1,6 @@
 """The five synthetic decode workloads, the multi-token decode (speculative
-verification) workloads built on them, and the KV-cache write workloads,
-named by what they are.
+verification) and replicated-segment workloads built on them, and the
+KV-cache write workloads, named by what they are.
 
 Length laws ("k" = 1024 tokens):
 * ``loguniform(a, b)``: L = floor(exp(U(ln a, ln b))), clipped to [a, b];
@@ -187,3 +187,37 @@ def get_verify_workload(name: str) -> VerifyWorkload:
     if name not in VERIFY_WORKLOADS:
         raise KeyError(f"unknown verify workload {name!r}; known: {sorted(VERIFY_WORKLOADS)}")
     return VERIFY_WORKLOADS[name]
+
+
+@dataclass(frozen=True)
+class SegmentWorkload:
+    """Decode with a replicated segment: each request also attends a window of
+    its last ``window`` tokens kept whole on every rank (a sliding-window
+    cache, new rows drawn independently), counted by rank ``seg_rank``."""
+    name: str
+    base: str
+    window: int
+    seg_rank: int = 0
+    description: str = ""
+
+    def geometry(self) -> Workload:
+        return WORKLOADS[self.base]
+
+
+SEGMENT_WORKLOADS = {
+    w.name: w
+    for w in [
+        SegmentWorkload(name="mla_bf16_longtail_sink_swa128", base="mla_bf16_longtail_sink", window=128,
+                        description="mla_bf16_longtail_sink batch (attention sink) plus a replicated 128-token "
+                                    "sliding window per request, counted on rank 0"),
+        SegmentWorkload(name="gqa_fp8_binned_swa128", base="gqa_fp8_binned", window=128, seg_rank=7,
+                        description="gqa_fp8_binned batch plus a replicated 128-token sliding window per request, "
+                                    "counted on rank 7"),
+    ]
+}
+
+
+def get_segment_workload(name: str) -> SegmentWorkload:
+    if name not in SEGMENT_WORKLOADS:
+        raise KeyError(f"unknown segment workload {name!r}; known: {sorted(SEGMENT_WORKLOADS)}")
+    return SEGMENT_WORKLOADS[name]

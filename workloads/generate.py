@@ -3,7 +3,7 @@
 Streams: ``numpy.random.SeedSequence(entropy=seed, spawn_key=(stream, i))``
 with stream 0 = lengths, 1 = block permutation, 2 = q, 3 = K, 4 = V,
 5 = fp8 scales and sinks, 6 = needles, 7 = KV-write contexts, 8 = the
-queries of multi-token decode. K and V are drawn per request, in
+queries of multi-token decode, 9 = replicated segments. K and V are drawn per request, in
 canonical (request-contiguous) token order, with a torch generator on the
 requested device, so large batches are produced in device memory; the stored
 values are what both the oracle (after a copy to the host) and the GPU path
@@ -30,7 +30,7 @@ import torch
 
 from .configs import KvWriteWorkload, Workload
 
-LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES, CONTEXT, VERIFYQ = range(9)
+LENGTHS, BLOCKPERM, QSTREAM, KSTREAM, VSTREAM, SCALES, NEEDLES, CONTEXT, VERIFYQ, SEGMENT = range(10)
 
 TORCH_FORMAT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
 
@@ -224,3 +224,37 @@ def make_verify_queries(w: Workload, batch: int, q_len: int, device="cpu") -> to
     multi-token decode of the last ``q_len`` tokens of each request."""
     q32 = _randn((batch, q_len, w.num_q_heads, w.head_dim_k), _seed(w.seed, VERIFYQ, q_len), device)
     return q32.to(TORCH_FORMAT[w.q_format])
+
+
+@dataclass
+class Segment:
+    """A replicated segment per request (e.g. the sliding-window cache): its
+    own tokens, stored in a one-rank paged pool of the workload's geometry."""
+    lens: np.ndarray              # [B] int32: min(L_b, window)
+    block_table: np.ndarray       # [B, max_vblocks] int32, -1 = unused
+    num_blocks: int
+    k: list                       # per request [lens_b, Hkv, Dk] in kv_format
+    v: list                       # per request [lens_b, Hkv, Dv], or None (MLA)
+
+
+def make_segment(w: Workload, seq_lens, window: int, k_scale=None, v_scale=None, device="cpu") -> Segment:
+    """Seeded segment rows ~ N(0, 1) (stream 9), ``min(L_b, window)`` tokens per
+    request, stored like the cache (same fp8 scales); block ids a seeded
+    permutation handed out in request order."""
+    lens = np.minimum(np.asarray(seq_lens, dtype=np.int64), window).astype(np.int32)
+    nvb = [(int(L) + w.block_size - 1) // w.block_size for L in lens]
+    nblk = max(1, int(sum(nvb)))
+    perm = _rng(w.seed, SEGMENT).permutation(nblk).astype(np.int32)
+    table = np.full((len(lens), max(nvb + [1])), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(nvb):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    ks, vs = [], []
+    for b, L in enumerate(lens):
+        kb = _randn((int(L), w.num_kv_heads, w.head_dim_k), _seed(w.seed, SEGMENT, 1 + 2 * b), device)
+        ks.append(_store(kb, w.kv_format, k_scale))
+        if not w.mla:
+            vb = _randn((int(L), w.num_kv_heads, w.head_dim_v), _seed(w.seed, SEGMENT, 2 + 2 * b), device)
+            vs.append(_store(vb, w.kv_format, v_scale))
+    return Segment(lens, table, nblk, ks, None if w.mla else vs)
