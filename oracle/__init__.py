@@ -18,14 +18,20 @@ What it computes, each function citing the passage it follows:
 * ``cache``     - the KV-cache write: new rows stored (fp32 as is, bf16 and fp8
                   e4m3 by nearest-value rounding, fp8 through the per-head
                   scale) at the slots the slot mapping gives, non-owners
-                  skipped ("Decode Context Parallel (DCP)", section "DCP slot
-                  mapping"; "DeepSeek V4.1 context parallelism", section
+                  skipped ("Decode Context Parallel (DCP)", section "KV-cache
+                  layout"; "DeepSeek V4.1 context parallelism", section
                   "Cache ownership").
+* ``gather``    - the context gather of (chunked) prefill: every cached
+                  position's stored row copied from its owner back into
+                  request-contiguous order ("Decode Context Parallel (DCP)",
+                  section "Prefill and chunked prefill").
 * ``attention`` - plain full-softmax decode attention over the *unsharded*
                   sequence in float64, the per-rank partial (O, LSE) over the
-                  tokens a rank owns, and the log-sum-exp merge with an
-                  attention sink applied once ("DeepSeek V4.1 context
-                  parallelism", section "Decode computation").
+                  tokens a rank owns, the log-sum-exp merge with an attention
+                  sink applied once, multi-token decode (causal among the last
+                  q_len tokens) and a replicated segment counted by one rank
+                  ("DeepSeek V4.1 context parallelism", section "Decode
+                  computation").
 
 Every function here is pinned by ``-m "not gpu"`` tests against something other
 than itself (hand-derived worked example, closed forms, invariants, torch's
@@ -34,4 +40,4 @@ the E4M3 code table's own values).
 No function is "parity unpinned".
 """
 
-from . import formats, layout, attention, cache  # noqa: F401
+from . import formats, layout, attention, cache, gather  # noqa: F401
