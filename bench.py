@@ -27,6 +27,10 @@ rank's partial attention, the fold of each request's W-token segment into
 the designated rank's partial, and the merge (sink once); ``value`` counts
 the sharded KV and the segments once.
 
+With ``--workload gather_<decode workload>`` a step is the chunked-prefill
+context gather of every request's whole cached sequence back into
+request-contiguous order (``value``: bytes read + written per second).
+
 With ``--workload kvw_*`` a step is instead the KV-cache write of a batch of
 new tokens (slot mapping, then the write of every row into its owner's pool);
 ``value`` and ``roofline`` then count the write's algorithmic bytes (new rows
@@ -51,10 +55,11 @@ DEFAULT_WORKLOAD = "gqa_fp8_binned"
 KV_WRITE_METRIC = "KV-cache write GB/s (new rows + slots read, stored rows written) at 1 GPU"
 VERIFY_METRIC = "multi-token decode KV GB/s (% of MI355X HBM peak) + verified tokens/s at 1 GPU"
 SEGMENT_METRIC = "decode with a replicated segment: KV GB/s (% of MI355X HBM peak) + merged queries/s at 1 GPU"
+GATHER_METRIC = "context gather GB/s (stored rows read + written) at 1 GPU"
 KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
-                "kv_write": "kv_write"}
+                "kv_write": "kv_write", "gather": "gather_context_kernel"}
 KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip",
-                  "kv_write": "kv_write.hip"}
+                  "kv_write": "kv_write.hip", "gather": "gather.hip"}
 
 
 def kernel_family(w):
@@ -527,6 +532,93 @@ def cpu_baseline_segment(case, seg, sw, budget_s):
     }
 
 
+def bench_gather(args, name):
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from tests.harness import DeviceInputs
+    from workloads import get_workload, make_case
+
+    w = get_workload(name[len("gather_"):])
+    if not w.mla:
+        print("the context gather is measured on MLA caches (a GQA cache keeps V transposed inside a block)",
+              file=sys.stderr)
+        sys.exit(2)
+    case = make_case(w, device="cuda")
+    inp = DeviceInputs(case, "cuda", fill="zero")
+    ctx = case.seq_lens.astype(np.int64)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int64)).cuda()
+    T = int(ctx.sum())
+    out = torch.empty((T, w.num_kv_heads, w.head_dim_k), dtype=inp.cache.dtype, device="cuda")
+    kv = inp.cache.descriptor(0)
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: {case.batch} requests, {T} context tokens, {case.kv_bytes() / 1e9:.3f} GB gathered",
+          file=sys.stderr, flush=True)
+
+    def step():
+        dcp.dcp_gather_context(kv, inp.D, inp.I, inp.block_table, cu, T, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = 2 * case.kv_bytes()  # every stored row read once and written once
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out_line = {
+        "metric": GATHER_METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "base": w.name, "requests": case.batch, "tokens": T,
+                   "bytes_per_token": 2 * w.kv_bytes_per_token(), "kernel": "gather_context_kernel",
+                   "tokens_per_s": round(T / (ms * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic("gather", name),
+                     "kernel_avg_ms": round(ms, 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out_line["cpu_baseline"] = cpu_baseline_gather(inp, case, args.cpu_budget_s)
+    print(json.dumps(out_line), flush=True)
+
+
+def cpu_baseline_gather(inp, case, budget_s):
+    """Time the oracle's gather on whole requests of the same pools (copied to the host)."""
+    import numpy as np
+    import torch
+    from oracle import gather as ogather
+    w = case.workload
+    kp = inp.cache.k.view(torch.int16).cpu().numpy()
+    order = np.random.default_rng(12345).permutation(case.batch)
+    spent, nbytes, done = 0.0, 0, []
+    for b in order:
+        ctx = np.zeros(case.batch, dtype=np.int64)
+        ctx[b] = int(case.seq_lens[b])
+        t0 = time.perf_counter()
+        ogather.gather_context(kp, None, inp.block_table_np, ctx, inp.bs, inp.D, inp.I)
+        spent += time.perf_counter() - t0
+        nbytes += 2 * int(ctx[b]) * w.kv_bytes_per_token()
+        done.append(int(b))
+        if spent >= budget_s:
+            break
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {case.batch} requests gathered one at a time by the oracle; {spent:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -570,6 +662,9 @@ def main():
         return
     if args.workload.startswith("kvw_"):
         bench_kv_write(args, args.workload)
+        return
+    if args.workload.startswith("gather_"):
+        bench_gather(args, args.workload)
         return
     from workloads import SEGMENT_WORKLOADS, VERIFY_WORKLOADS
     if args.workload in VERIFY_WORKLOADS:

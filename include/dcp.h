@@ -378,6 +378,44 @@ int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, 
                        const int64_t* slots, int32_t num_ranks, const dcp_kv_cache_t* kv, void* stream);
 
 /*
+ * dcp_gather_context - (chunked) prefill: gather each request's cached
+ * context from the ranks' shards back into request-contiguous order.
+ *
+ * Source: "Decode Context Parallel (DCP)", section "Prefill and chunked
+ * prefill" (MLA gathers the context KV cache and restores request-contiguous
+ * order before the current query chunk attends it); "DeepSeek V4.1 context
+ * parallelism", section "Cache ownership" (pages are copied as stored,
+ * without dequantising).
+ *
+ * Request b's context is its positions 0 .. cu_ctx[b+1] - cu_ctx[b] - 1.
+ * Output row t = cu_ctx[b] + x holds the stored K row (and V row) of
+ * position x of request b, copied bit for bit from the pool of its owner
+ * ((x / interleave) % dcp_size) at the slot dcp_slot_mapping gives (block
+ * block_table[b][x / (block_size * dcp_size)], shared by all ranks). A
+ * position whose virtual block is >= max_vblocks or has a negative block id
+ * gives a zero row.
+ *
+ * kv          the dcp_size pools, counted from the pool kv->k points to;
+ *             rows must be contiguous (dim stride 1) and 16-byte aligned
+ *             (head_dim * element size a multiple of 16)
+ * block_table device, int32, row b at block_table + b * block_table_stride
+ * cu_ctx      device, [num_reqs + 1] int64, cu_ctx[0] = 0, non-decreasing
+ * total_tokens = cu_ctx[num_reqs] (the host knows it from the batch plan)
+ * out_k       device, [total_tokens, num_kv_heads, head_dim_k], kv->dtype
+ * out_v       device, [total_tokens, num_kv_heads, head_dim_v], or NULL (K
+ *             only; must be NULL when kv->v is NULL: MLA gathers the latent
+ *             row, which holds the value)
+ * Errors: DCP_ERR_INVALID_ARG (sizes, relations, NULL pointers, out_v with
+ * kv->v == NULL), DCP_ERR_UNSUPPORTED (dtype, a row layout that is not
+ * contiguous and 16-byte aligned, more than 4095 16-byte chunks per token),
+ * DCP_ERR_HIP.
+ */
+int dcp_gather_context(const dcp_kv_cache_t* kv, int32_t dcp_size, int32_t interleave,
+                       const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
+                       int32_t max_vblocks, const int64_t* cu_ctx, int64_t total_tokens,
+                       void* out_k, void* out_v, void* stream);
+
+/*
  * Measurement hook for benchmarks.
  *
  * dcp_profile_enable(1) makes every following dcp_partial_decode_attn and

@@ -344,6 +344,28 @@ int dcp_profile_collect(double* total_ms, int32_t* launches) {
   return DCP_OK;
 }
 
+int dcp_gather_context(const dcp_kv_cache_t* kv, int32_t dcp_size, int32_t interleave, const int32_t* block_table,
+                       int32_t num_reqs, int64_t block_table_stride, int32_t max_vblocks, const int64_t* cu_ctx,
+                       int64_t total_tokens, void* out_k, void* out_v, void* stream) {
+  if (!kv) return DCP_ERR_INVALID_ARG;
+  if (int st = check_layout_args(kv->block_size, dcp_size, interleave)) return st;
+  if (!valid_dtype(kv->dtype)) return DCP_ERR_UNSUPPORTED;
+  if (num_reqs < 0 || total_tokens < 0 || max_vblocks < 0 || block_table_stride < max_vblocks)
+    return DCP_ERR_INVALID_ARG;
+  if (kv->num_kv_heads < 1 || kv->head_dim_k < 1 || kv->head_dim_v < 1 || kv->num_blocks < 1)
+    return DCP_ERR_INVALID_ARG;
+  if (out_v && !kv->v) return DCP_ERR_INVALID_ARG;  // MLA: the value is part of the gathered K row
+  if (total_tokens == 0) return DCP_OK;
+  if (num_reqs == 0 || !cu_ctx || !out_k || !kv->k) return DCP_ERR_INVALID_ARG;
+  if (max_vblocks > 0 && !block_table) return DCP_ERR_INVALID_ARG;
+  if (total_tokens >= (int64_t(1) << 37)) return DCP_ERR_INVALID_ARG;
+  if (!gather_supported(*kv, out_v != nullptr)) return DCP_ERR_UNSUPPORTED;
+  return launch_gather_context(*kv, dcp_size, interleave, block_table, num_reqs, block_table_stride, max_vblocks,
+                               cu_ctx, total_tokens, out_k, out_v, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DCP_OK
+             : DCP_ERR_HIP;
+}
+
 int dcp_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype, int64_t num_tokens,
                        const int64_t* slots, int32_t num_ranks, const dcp_kv_cache_t* kv, void* stream) {
   if (!kv || num_tokens < 0 || num_ranks < 1) return DCP_ERR_INVALID_ARG;

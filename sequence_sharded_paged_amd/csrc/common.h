@@ -61,6 +61,10 @@ hipError_t launch_slot_mapping(const int64_t* positions, const int32_t* req_indi
                                int interleave, int64_t* slots, hipStream_t s);
 hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_bf16, int64_t num_tokens,
                            const int64_t* slots, int num_ranks, const dcp_kv_cache_t& kv, hipStream_t stream);
+bool gather_supported(const dcp_kv_cache_t& kv, bool with_v);
+hipError_t launch_gather_context(const dcp_kv_cache_t& kv, int dcp_size, int interleave, const int32_t* block_table,
+                                 int num_reqs, int64_t bt_stride, int max_vblocks, const int64_t* cu_ctx,
+                                 int64_t total, void* out_k, void* out_v, hipStream_t stream);
 hipError_t launch_lse_fold(float* o, float* lse, const float* o_add, const float* lse_add, int64_t rows,
                            int head_dim_v, hipStream_t s);
 hipError_t launch_lse_merge(const float* part_o, const float* part_lse, int num_parts, int batch,

@@ -24,7 +24,7 @@ EXPORTS = [
     "dcp_abi_version", "dcp_status_string", "dcp_local_seq_lens", "dcp_slot_mapping",
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
     "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
-    "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn",
+    "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn", "dcp_gather_context",
     "dcp_profile_enable", "dcp_profile_collect",
 ]
 
@@ -86,6 +86,8 @@ def lib():
         L.dcp_partial_segment_attn.restype = ctypes.c_int
         L.dcp_partial_segment_attn.argtypes = [vp, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp, f32, i32,
                                                i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dcp_gather_context.restype = ctypes.c_int
+        L.dcp_gather_context.argtypes = [ctypes.POINTER(KvCache), i32, i32, vp, i32, i64, i32, vp, i64, vp, vp, vp]
         L.dcp_kv_cache_write.restype = ctypes.c_int
         L.dcp_kv_cache_write.argtypes = [vp, vp, i32, i64, vp, i32, ctypes.POINTER(KvCache), vp]
         L.dcp_profile_enable.restype = ctypes.c_int
@@ -262,6 +264,21 @@ def dcp_kv_cache_write(k_new, v_new, slots, kv: KvCache, stream=None):
     _check("dcp_kv_cache_write", lib().dcp_kv_cache_write(
         _ptr(k_new), _ptr(v_new), TORCH_TO_DCP[k_new.dtype], T, _ptr(slots), R, ctypes.byref(kv),
         _stream(stream)))
+
+
+def dcp_gather_context(kv: KvCache, dcp_size, interleave, block_table, cu_ctx, total_tokens, out_k, out_v=None,
+                       max_vblocks=None, stream=None):
+    """Gather every request's context (``cu_ctx [B+1]`` int64 offsets) from the
+    ``dcp_size`` pools ``kv`` describes into ``out_k [T, Hkv, Dk]`` (and
+    ``out_v``) in request-then-position order, stored bits copied."""
+    assert cu_ctx.dtype == torch.int64 and cu_ctx.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.stride(1) == 1
+    assert out_k.is_contiguous() and (out_v is None or out_v.is_contiguous())
+    if max_vblocks is None:
+        max_vblocks = block_table.shape[1]
+    _check("dcp_gather_context", lib().dcp_gather_context(
+        ctypes.byref(kv), dcp_size, interleave, _ptr(block_table), block_table.shape[0], block_table.stride(0),
+        max_vblocks, _ptr(cu_ctx), int(total_tokens), _ptr(out_k), _ptr(out_v), _stream(stream)))
 
 
 def dcp_profile_enable(on: bool = True):

@@ -210,3 +210,24 @@ def test_segment_validation(L):
     assert call(part=NULL) == INV
     assert call(ws_bytes=16) == WS
     assert call(batch=0) == 0
+
+
+def test_gather_validation(L):
+    p = _fake(64)
+    f = L.dcp_gather_context
+    kv = _kv()
+
+    def call(kv=kv, D=4, I=1, nreq=2, stride=4, maxvb=4, cu=p, total=100, out_k=p, out_v=NULL):
+        return f(ctypes.byref(kv), D, I, p, nreq, stride, maxvb, cu, total, out_k, out_v, NULL)
+
+    assert call(I=3) == INV                                # block_size 16 % 3
+    assert call(stride=2) == INV                           # stride < max_vblocks
+    assert call(total=-1) == INV
+    assert call(cu=NULL) == INV
+    assert call(out_k=NULL) == INV
+    assert call(nreq=0) == INV                             # tokens but no request
+    assert call(kv=_kv(v=None, head_dim_v=64), out_v=p) == INV   # MLA: no V output
+    assert call(kv=_kv(dtype=9)) == UNS
+    assert call(out_v=p) == UNS                            # V transposed inside a block
+    assert call(kv=_kv(head_dim_k=4)) == UNS               # rows under 16 bytes
+    assert call(total=0, cu=NULL, out_k=NULL) == 0         # nothing to gather
