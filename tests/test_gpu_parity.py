@@ -214,6 +214,18 @@ def test_large_logit_needles(device, name):
         check_against_oracle(inp, inp.run(algo=algo))
 
 
+def test_mla_replay_in_later_unit(device):
+    """Many short requests (about four tiles per rank), each with a needle
+    scored ~120 above the rest at its last token: stream-K workers span many
+    units, and pieces several units past a worker's first one outgrow their
+    reference max and are replayed. The replay restarts the DMA walker there."""
+    w = get_workload("mla_bf16_bimodal")
+    lens = [1000 + 37 * (b % 7) for b in range(80)]
+    case = make_case(w, device=device, seq_lens=lens, needles=1, needle_logit=120.0)
+    inp = DeviceInputs(case, device)
+    check_against_oracle(inp, inp.run(algo=FAST), requests=list(range(0, 80, 9)))
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_bimodal"])
 def test_moderate_needles(device, name):
     """Needles at logit ~20 on every rank: a misplaced or dropped block shows
