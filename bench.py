@@ -139,7 +139,7 @@ def kv_write_kernels(w):
     """The kernels one dcp_kv_cache_write call launches for this workload."""
     if w.tokens < 1024:
         return ["kv_scatter_kernel"]
-    return ["kv_rows_kernel"] + ([] if w.geometry().mla else ["kv_vt_kernel"])
+    return ["kv_rows_kernel"] + ([] if w.geometry().mla else ["kv_vt16_kernel"])
 
 
 def cpu_baseline_kv_write(case, budget_s):

@@ -39,15 +39,17 @@ __device__ __forceinline__ float quotient(float x, double r) {
 }
 
 // fp32 -> E4M3 codes of eight values: round to nearest, ties to even
-// (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950), after clamping to +-448 so that
-// larger magnitudes and infinities saturate; NaN -> 0x7F.
+// (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950), after clamping to +-448 (v_med3_f32)
+// so that larger magnitudes and infinities saturate; NaN -> 0x7F (whatever the
+// clamp and the conversion made of a NaN is replaced; a lane takes that branch
+// only when one of its eight values is a NaN).
 __device__ __forceinline__ void e4m3_codes(const float (&q)[8], uint32_t (&code)[8]) {
-  uint32_t nan = 0;
+  bool any_nan = false;
   float c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    nan |= ((__float_as_uint(q[i]) & 0x7fffffffu) > 0x7f800000u) << i;
-    c[i] = fminf(fmaxf(q[i], -448.0f), 448.0f);
+    any_nan |= __builtin_isnan(q[i]);
+    c[i] = __builtin_amdgcn_fmed3f(q[i], -448.0f, 448.0f);
   }
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
@@ -55,10 +57,10 @@ __device__ __forceinline__ void e4m3_codes(const float (&q)[8], uint32_t (&code)
     code[i] = w & 0xffu;
     code[i + 1] = (w >> 8) & 0xffu;
   }
-  if (nan) {
+  if (any_nan) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if ((nan >> i) & 1u) code[i] = 0x7fu;
+      if (__builtin_isnan(q[i])) code[i] = 0x7fu;
   }
 }
 
@@ -160,6 +162,7 @@ struct KvWriteParams {
   int vec_k, vec_v;      // 1: the pool's 8-element chunks are contiguous and aligned (vector stores)
   int v_transposed;      // 1: V is token-contiguous inside a block (kv_vt_kernel)
   int vt_quads;          // kv_vt_kernel may store an aligned word of 4 slots as one vector
+  int vt_vec16;          // kv_vt16_kernel: 16-byte words of slots stay aligned across heads and dims
   int rank_lanes;        // kv_rows_kernel: lanes per token, a power of two >= num_ranks
 };
 
@@ -472,6 +475,248 @@ __global__ void __launch_bounds__(256) kv_vt_kernel(KvWriteParams p) {
   }
 }
 
+// Large batches, V stored token-contiguous inside a block, with 16-byte
+// words of slots aligned across heads and dims (the common case): as
+// kv_vt_kernel, but the tokens are grouped by the 16-byte pool word their slot
+// falls in (16 fp8 / 8 bf16 / 4 fp32 slots), and the converted tile sits in
+// LDS as [dim][group] 16-byte cells, so a word whose slots are all written
+// leaves LDS with one 16-byte read and reaches the pool with one 16-byte store
+// (consecutive words of a block row by consecutive lanes). Up to kVtGroups
+// groups are staged at a time; tiles with more (scattered slots) take several
+// rounds per head. The cell of group g in dim row d is g ^ ((d / 8) % 8): the
+// sixteen lanes that convert one token's row write rows eight apart, and the
+// swizzle spreads them over the banks.
+constexpr int kVtGroups = 8;  // 16-byte word groups staged in LDS at a time
+
+template <int kW>
+__device__ __forceinline__ int vt16_group_pass(const KvWriteParams& p, int lane, int ntok, uint64_t f,
+                                               uint32_t* s_gmask, int64_t* s_gbase, int* s_col, int* s_groups) {
+  constexpr int kLog = kW == 16 ? 4 : kW == 8 ? 3 : 2;
+  const bool valid = lane < ntok && f != ~uint64_t(0);
+  int64_t vr = 0;
+  if (valid) {
+    const int rk = static_cast<int>(f >> kSlotBits);
+    const int64_t s = static_cast<int64_t>(f & ((uint64_t(1) << kSlotBits) - 1));
+    const int64_t blk = s / p.kv.block_size, off = s - blk * p.kv.block_size;
+    vr = rk * p.kv.v_stride[0] + blk * p.kv.v_stride[1] + off * p.kv.v_stride[3];
+  }
+  const uint64_t vmask = __builtin_amdgcn_ballot_w64(valid);
+  const int nvalid = __builtin_popcountll(vmask);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int rank;  // position in the order (valid first, by offset, ties by token)
+  if (valid) {
+    rank = 0;
+    for (uint64_t m = vmask; m; m &= m - 1) {
+      const int jl = __builtin_ctzll(m);
+      const int64_t vj = __shfl(vr, jl, 64);
+      rank += (vj < vr) || (vj == vr && jl < lane);
+    }
+  } else {
+    rank = nvalid + __builtin_popcountll(~vmask & below);
+  }
+  const int tok = __builtin_amdgcn_ds_permute(rank * 4, lane);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr >> 32)));
+  const int64_t vs = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  const int64_t word = vs >> kLog;
+  const int64_t prev = __shfl(word, lane == 0 ? 0 : lane - 1, 64);
+  const bool in = lane < nvalid;
+  const uint64_t starts = __builtin_amdgcn_ballot_w64(in && (lane == 0 || word != prev));
+  const int g = __builtin_popcountll(starts & ((below << 1) | 1)) - 1;
+  s_gmask[lane] = 0;
+  s_col[lane] = -1;
+  __builtin_amdgcn_wave_barrier();
+  if (in) {
+    const int u = static_cast<int>(vs & (kW - 1));
+    atomicOr(&s_gmask[g], 1u << u);
+    s_col[tok] = kW * g + u;
+    if ((starts >> lane) & 1) s_gbase[g] = word * kW;
+  }
+  if (lane == 0) *s_groups = __builtin_popcountll(starts);
+  return nvalid;
+}
+
+template <int kDst, bool kSrcBf16>
+__global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
+  using St = typename Stored<kDst>::T;
+  constexpr int kW = 16 / static_cast<int>(sizeof(St));  // slots per 16-byte word
+  __shared__ uint64_t s_owners[kVtTokens];    // owners not yet written, per token
+  __shared__ uint64_t s_first[kVtTokens];     // (first owner << kSlotBits) | its slot; all ones: none
+  __shared__ uint32_t s_gmask[kVtTokens];     // slots of group g's word that a token of the pass writes
+  __shared__ int64_t s_gbase[kVtTokens];      // first element of group g's word (head 0, dim 0)
+  __shared__ int s_col[kVtTokens];            // token -> kW * group + slot, or -1
+  __shared__ int s_groups;
+  __shared__ uint4 s_cell[kVtDims * kVtGroups];  // [dim][group ^ swizzle], 16 KB
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t T = p.num_tokens;
+  const int64_t tiles = (T + kVtTokens - 1) / kVtTokens;
+  const int64_t per = gridDim.x / kXcds;
+  const int64_t tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= tiles) return;
+  const int64_t t0 = tile * kVtTokens;
+  const int ntok = static_cast<int>(T - t0 < kVtTokens ? T - t0 : kVtTokens);
+  const int H = p.kv.num_kv_heads, dv = p.kv.head_dim_v;
+  const int ds = blockIdx.y * kVtDims;
+  const int nd = dv - ds < kVtDims ? dv - ds : kVtDims;
+  const int cpt = nd / 8, total = ntok * cpt;  // <= 1024
+  const int64_t cap = static_cast<int64_t>(p.kv.num_blocks) * p.kv.block_size;
+  St* vpool = static_cast<St*>(const_cast<void*>(p.kv.v));
+  const int64_t vdim = p.kv.v_stride[4], vhead = p.kv.v_stride[2];
+  char* cells = reinterpret_cast<char*>(s_cell);
+  // this thread's chunks (token, first dim), fixed for the whole tile (-1: none)
+  int ck_tok[4], ck_d0[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = k * 256 + tid;
+    const int i = c / cpt;
+    ck_tok[k] = c < total ? i : -1;
+    ck_d0[k] = (c - i * cpt) * 8;
+  }
+
+  auto load_head = [&](int h, Raw8<kSrcBf16> (&raw)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (ck_tok[k] >= 0) raw[k] = load8<kSrcBf16>(p.v_new, ((t0 + ck_tok[k]) * H + h) * dv + ds + ck_d0[k]);
+  };
+  // converted elements of the tokens in groups g0 .. g0 + kVtGroups - 1 into their cells
+  auto to_lds = [&](int h, const Raw8<kSrcBf16> (&raw)[4], int g0) __attribute__((always_inline)) {
+    double rcp = 1.0;
+    if constexpr (kDst == DCP_FP8_E4M3) rcp = scale_rcp(p.kv.v_scale, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = ck_tok[k], d0 = ck_d0[k];
+      if (i < 0) continue;
+      const int col = s_col[i];
+      const int gb = (col >= 0 ? col / kW : -1) - g0;
+      if (col < 0 || gb < 0 || gb >= kVtGroups) continue;
+      uint32_t q[8];
+      convert8<kDst, kSrcBf16>(raw[k], rcp, q);
+      const int u = col - (col / kW) * kW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + e;
+        *reinterpret_cast<St*>(cells + (d * kVtGroups + (gb ^ ((d >> 3) & 7))) * 16 + u * sizeof(St)) =
+            static_cast<St>(q[e]);
+      }
+    }
+  };
+  // thread = (group gb, dim), the groups of the round rounded up to a power of two
+  auto store_cells = [&](int h, int g0) __attribute__((always_inline)) {
+    const int ng = min(s_groups - g0, kVtGroups);
+    int gp = 1;
+    while (gp < ng) gp *= 2;
+    const int gb = tid & (gp - 1);
+    if (gb >= ng) return;
+    const int g = g0 + gb;
+    const uint32_t mask = s_gmask[g];
+    const bool full = mask == (kW == 32 ? ~0u : (1u << kW) - 1);
+    const int64_t base = s_gbase[g] + h * vhead;
+    for (int d = tid / gp; d < nd; d += 256 / gp) {
+      const uint4 v = s_cell[d * kVtGroups + (gb ^ ((d >> 3) & 7))];
+      St* dst = vpool + base + static_cast<int64_t>(ds + d) * vdim;
+      if (full) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        // the written slots in the widest aligned pieces they fill: 8 bytes,
+        // 4 bytes, then single elements (a run of slots leaves at most a
+        // ragged piece at each end)
+        const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+        const St* el = reinterpret_cast<const St*>(&v);
+        constexpr int kHalf = kW / 2, kQuad = 4 / static_cast<int>(sizeof(St));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t hm = (mask >> (hh * kHalf)) & ((1u << kHalf) - 1);
+          if (hm == (1u << kHalf) - 1) {
+            *reinterpret_cast<uint2*>(dst + hh * kHalf) = uint2{dw[2 * hh], dw[2 * hh + 1]};
+            continue;
+          }
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int u0 = hh * kHalf + qq * kQuad;
+            const uint32_t qm = (mask >> u0) & ((1u << kQuad) - 1);
+            if (qm == (1u << kQuad) - 1) {
+              *reinterpret_cast<uint32_t*>(dst + u0) = dw[2 * hh + qq];
+            } else if (qm) {
+#pragma unroll
+              for (int u = u0; u < u0 + kQuad; ++u)
+                if ((mask >> u) & 1u) dst[u] = el[u];
+            }
+          }
+        }
+      }
+    }
+  };
+  // all heads of one owner pass, one round of up to kVtGroups groups at a
+  // time (one round unless the slots are scattered); within a round the next
+  // head's rows load while this one is stored
+  // Two register buffers: head h + 1's rows are requested before head h is
+  // converted, so their latency hides behind the conversion and the stores.
+  auto head_step = [&](int h, int g0, const Raw8<kSrcBf16> (&cur)[4], Raw8<kSrcBf16> (&nxt)[4])
+      __attribute__((always_inline)) {
+    if (h + 1 < H) load_head(h + 1, nxt);
+    to_lds(h, cur, g0);
+    __syncthreads();
+    store_cells(h, g0);
+    __syncthreads();
+  };
+  auto heads = [&](Raw8<kSrcBf16> (&raw)[4], bool preloaded) __attribute__((always_inline)) {
+    const int groups = s_groups;
+    Raw8<kSrcBf16> alt[4];
+    for (int g0 = 0; g0 < groups; g0 += kVtGroups) {
+      if (g0 > 0 || !preloaded) load_head(0, raw);
+      for (int h = 0; h < H; h += 2) {
+        head_step(h, g0, raw, alt);
+        if (h + 1 < H) head_step(h + 1, g0, alt, raw);
+      }
+    }
+  };
+
+  Raw8<kSrcBf16> raw[4];
+  load_head(0, raw);
+  if (tid < kVtTokens) {
+    s_owners[tid] = 0;
+    s_first[tid] = ~uint64_t(0);
+  }
+  __syncthreads();
+  for (int pr = tid; pr < kVtTokens * p.num_ranks; pr += 256) {  // (token, rank) pairs
+    const int rk = pr / kVtTokens, i = pr - rk * kVtTokens;
+    if (i >= ntok) continue;
+    const int64_t s = p.slots[rk * T + t0 + i];
+    if (s >= 0 && s < cap) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&s_owners[i]), 1ull << rk);
+      atomicMin(reinterpret_cast<unsigned long long*>(&s_first[i]),
+                (static_cast<unsigned long long>(rk) << kSlotBits) | static_cast<unsigned long long>(s));
+    }
+  }
+  __syncthreads();
+  int any = 0;
+  if (wave == 0) {
+    const uint64_t f = s_first[lane];
+    if (f != ~uint64_t(0)) s_owners[lane] &= ~(uint64_t(1) << (f >> kSlotBits));
+    any = vt16_group_pass<kW>(p, lane, ntok, f, s_gmask, s_gbase, s_col, &s_groups) > 0;
+  }
+  if (!__syncthreads_or(any)) return;  // no token of the tile has an owner
+  heads(raw, true);
+
+  // further owners (a token kept on more than one rank)
+  for (;;) {
+    any = 0;
+    if (wave == 0) {
+      const uint64_t m = s_owners[lane];
+      uint64_t f = ~uint64_t(0);
+      if (m) {
+        const int rk = __builtin_ctzll(m);
+        s_owners[lane] = m & (m - 1);
+        f = (static_cast<uint64_t>(rk) << kSlotBits) | static_cast<uint64_t>(p.slots[rk * T + t0 + lane]);
+      }
+      any = vt16_group_pass<kW>(p, lane, ntok, f, s_gmask, s_gbase, s_col, &s_groups) > 0;
+    }
+    if (!__syncthreads_or(any)) break;
+    heads(raw, false);
+  }
+}
+
 // Small batches (a decode step writes one token per request): one wavefront
 // per (token, KV head). Lane r < num_ranks reads the token's slot on rank r
 // while the lanes' source loads are in flight; each lane then converts its
@@ -581,7 +826,8 @@ static void launch_typed(const KvWriteParams& p, hipStream_t stream) {
   const int64_t tiles = (T + kVtTokens - 1) / kVtTokens;
   const dim3 grid(static_cast<unsigned>((tiles + kXcds - 1) / kXcds * kXcds),
                   static_cast<unsigned>((p.kv.head_dim_v + kVtDims - 1) / kVtDims));
-  hipLaunchKernelGGL((kv_vt_kernel<kDst, kSrcBf16>), grid, dim3(256), 0, stream, p);
+  if (p.vt_vec16) hipLaunchKernelGGL((kv_vt16_kernel<kDst, kSrcBf16>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((kv_vt_kernel<kDst, kSrcBf16>), grid, dim3(256), 0, stream, p);
 }
 
 template <int kDst>
@@ -605,6 +851,9 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_bf16, i
   p.v_transposed = kv.v && kv.v_stride[3] == 1 && kv.v_stride[4] != 1;
   p.vt_quads = p.v_transposed && kv.v_stride[4] % 4 == 0 && kv.v_stride[2] % 4 == 0 &&
                reinterpret_cast<uintptr_t>(kv.v) % static_cast<uintptr_t>(4 * eb) == 0;
+  const int w16 = 16 / eb;  // slots per 16-byte word
+  p.vt_vec16 = p.v_transposed && kv.v_stride[4] % w16 == 0 && kv.v_stride[2] % w16 == 0 &&
+               reinterpret_cast<uintptr_t>(kv.v) % 16 == 0;
   p.rank_lanes = 1;
   while (p.rank_lanes < num_ranks) p.rank_lanes *= 2;
   if (kv.dtype == DCP_FP8_E4M3) launch_for<DCP_FP8_E4M3>(p, src_bf16, stream);
