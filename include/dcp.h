@@ -83,6 +83,38 @@ int dcp_local_seq_lens(const int32_t* seq_lens, int32_t num_reqs, int32_t block_
                        void* stream);
 
 /*
+ * dcp_check_block_table - count the block-table entries in use that break the
+ * device-data contract. A checking aid: the attention, write and gather calls
+ * do not check block ids, and an id outside the pool makes them read or write
+ * outside it.
+ *
+ * Source: "Decode Context Parallel (DCP)", section "KV-cache layout" (a
+ * virtual block spans block_size * dcp_size positions; one table row per
+ * request holds a physical block id per virtual block, shared by the ranks).
+ *
+ * Request b with length L = max(seq_lens[b], 0) uses virtual blocks vb = 0 ..
+ * ceil(L / (block_size * dcp_size)) - 1. *bad_count receives the number of
+ * those (b, vb) with vb >= max_vblocks (entries the table lacks) or with
+ * block_table[b * block_table_stride + vb] outside [0, num_blocks), saturated
+ * at INT32_MAX. 0 means the table is valid for these lengths.
+ *
+ * block_table        device, int32, row b at block_table + b * block_table_stride
+ * num_reqs           rows, >= 0
+ * block_table_stride >= max_vblocks
+ * max_vblocks        >= 0, valid columns per row
+ * seq_lens           device, [num_reqs] int32
+ * block_size, dcp_size >= 1; num_blocks >= 0 (physical blocks per rank pool)
+ * bad_count          device, one int32, overwritten (also when num_reqs == 0)
+ * Two kernels (clear, count); nothing is allocated.
+ * Errors: DCP_ERR_INVALID_ARG for a bad size or relation or a NULL pointer
+ * (block_table may be NULL when num_reqs or max_vblocks is 0; seq_lens when
+ * num_reqs is 0); DCP_ERR_HIP if a launch fails.
+ */
+int dcp_check_block_table(const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
+                          int32_t max_vblocks, const int32_t* seq_lens, int32_t block_size,
+                          int32_t dcp_size, int32_t num_blocks, int32_t* bad_count, void* stream);
+
+/*
  * dcp_slot_mapping - where each new token's KV goes on each rank.
  *
  * Source: "Decode Context Parallel (DCP)", section "KV-cache layout" (a

@@ -160,6 +160,21 @@ int dcp_local_seq_lens(const int32_t* seq_lens, int32_t num_reqs, int32_t block_
                                static_cast<hipStream_t>(stream)) == hipSuccess ? DCP_OK : DCP_ERR_HIP;
 }
 
+int dcp_check_block_table(const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
+                          int32_t max_vblocks, const int32_t* seq_lens, int32_t block_size, int32_t dcp_size,
+                          int32_t num_blocks, int32_t* bad_count, void* stream) {
+  if (block_size < 1 || dcp_size < 1 || num_reqs < 0 || max_vblocks < 0 || num_blocks < 0 ||
+      block_table_stride < max_vblocks)
+    return DCP_ERR_INVALID_ARG;
+  if (!bad_count) return DCP_ERR_INVALID_ARG;
+  if (num_reqs > 0 && !seq_lens) return DCP_ERR_INVALID_ARG;
+  if (num_reqs > 0 && max_vblocks > 0 && !block_table) return DCP_ERR_INVALID_ARG;
+  return launch_check_block_table(block_table, num_reqs, block_table_stride, max_vblocks, seq_lens, block_size,
+                                  dcp_size, num_blocks, bad_count, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DCP_OK
+             : DCP_ERR_HIP;
+}
+
 int dcp_slot_mapping(const int64_t* positions, const int32_t* req_indices, int64_t num_tokens,
                      const int32_t* block_table, int32_t num_reqs, int64_t block_table_stride,
                      int32_t max_vblocks, int32_t block_size, int32_t dcp_size, int32_t interleave,

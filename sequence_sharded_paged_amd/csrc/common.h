@@ -53,6 +53,9 @@ hipError_t launch_generic_attn(const AttnParams& p);
 hipError_t launch_gqa_attn(const AttnParams& p);
 hipError_t launch_mla_attn(const AttnParams& p);
 
+hipError_t launch_check_block_table(const int32_t* bt, int num_reqs, int64_t bt_stride, int max_vblocks,
+                                    const int32_t* seq_lens, int block_size, int dcp_size, int num_blocks,
+                                    int32_t* bad, hipStream_t s);
 hipError_t launch_local_seq_lens(const int32_t* seq_lens, int num_reqs, int dcp_size,
                                  int interleave, int32_t* local_lens, hipStream_t s);
 hipError_t launch_slot_mapping(const int64_t* positions, const int32_t* req_indices,

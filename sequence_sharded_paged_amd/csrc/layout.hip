@@ -58,6 +58,49 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(
   for (int r = 0; r < dcp_size; ++r) slots[static_cast<int64_t>(r) * num_tokens + t] = (r == owner) ? slot : -1;
 }
 
+// Block-table check: one workgroup per request counts the virtual blocks its
+// length needs whose entry is missing (vb >= max_vblocks) or outside the pool;
+// a wavefront reduction, then one atomic add per wavefront.
+__global__ void check_clear_kernel(int32_t* bad) { *bad = 0; }
+
+__global__ void __launch_bounds__(256) check_block_table_kernel(const int32_t* __restrict__ bt, int64_t bt_stride,
+                                                              int max_vblocks, const int32_t* __restrict__ seq_lens,
+                                                              int64_t span, int num_blocks, int32_t* bad) {
+  const int b = blockIdx.x;
+  const int64_t len = seq_lens[b] > 0 ? seq_lens[b] : 0;
+  const int64_t need = (len + span - 1) / span;
+  const int64_t have = need < max_vblocks ? need : max_vblocks;
+  int64_t n = 0;
+  for (int64_t vb = threadIdx.x; vb < have; vb += blockDim.x) {
+    const int32_t id = bt[b * bt_stride + vb];
+    n += (id < 0 || id >= num_blocks) ? 1 : 0;
+  }
+  if (threadIdx.x == 0) n += need - have;  // entries the table lacks
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_down(n, off, 64);
+  if ((threadIdx.x & 63) == 0 && n > 0) {
+    // add, saturating at INT32_MAX: a compare-and-swap loop (a failed swap
+    // means another wavefront's single addition landed, so it ends)
+    int32_t cur = atomicAdd(bad, 0);
+    for (;;) {
+      const int64_t sum = static_cast<int64_t>(cur) + n;
+      const int32_t next = sum > INT32_MAX ? INT32_MAX : static_cast<int32_t>(sum);
+      const int32_t prev = atomicCAS(bad, cur, next);
+      if (prev == cur) break;
+      cur = prev;
+    }
+  }
+}
+
+hipError_t launch_check_block_table(const int32_t* bt, int num_reqs, int64_t bt_stride, int max_vblocks,
+                                    const int32_t* seq_lens, int block_size, int dcp_size, int num_blocks,
+                                    int32_t* bad, hipStream_t s) {
+  hipLaunchKernelGGL(check_clear_kernel, dim3(1), dim3(1), 0, s, bad);
+  if (num_reqs > 0)
+    hipLaunchKernelGGL(check_block_table_kernel, dim3(static_cast<unsigned>(num_reqs)), dim3(256), 0, s, bt, bt_stride,
+                       max_vblocks, seq_lens, static_cast<int64_t>(block_size) * dcp_size, num_blocks, bad);
+  return hipGetLastError();
+}
+
 hipError_t launch_local_seq_lens(const int32_t* seq_lens, int num_reqs, int dcp_size, int interleave,
                                  int32_t* local_lens, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(num_reqs) * dcp_size;

@@ -25,7 +25,7 @@ EXPORTS = [
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
     "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
     "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn", "dcp_gather_context",
-    "dcp_profile_enable", "dcp_profile_collect",
+    "dcp_profile_enable", "dcp_profile_collect", "dcp_check_block_table",
 ]
 
 
@@ -90,6 +90,8 @@ def lib():
         L.dcp_gather_context.argtypes = [ctypes.POINTER(KvCache), i32, i32, vp, i32, i64, i32, vp, i64, vp, vp, vp]
         L.dcp_kv_cache_write.restype = ctypes.c_int
         L.dcp_kv_cache_write.argtypes = [vp, vp, i32, i64, vp, i32, ctypes.POINTER(KvCache), vp]
+        L.dcp_check_block_table.restype = ctypes.c_int
+        L.dcp_check_block_table.argtypes = [vp, i32, i64, i32, vp, i32, i32, i32, vp, vp]
         L.dcp_profile_enable.restype = ctypes.c_int
         L.dcp_profile_enable.argtypes = [ctypes.c_int]
         L.dcp_profile_collect.restype = ctypes.c_int
@@ -132,6 +134,24 @@ def dcp_local_seq_lens(seq_lens, block_size, dcp_size, interleave, out=None, str
         out = torch.empty((B, dcp_size), dtype=torch.int32, device=seq_lens.device)
     _check("dcp_local_seq_lens", lib().dcp_local_seq_lens(
         _ptr(seq_lens), B, block_size, dcp_size, interleave, _ptr(out), _stream(stream)))
+    return out
+
+
+def dcp_check_block_table(block_table, seq_lens, block_size, dcp_size, num_blocks, max_vblocks=None, out=None,
+                          stream=None):
+    """Count the in-use entries of ``block_table [B, >= max_vblocks] int32``
+    (device) that are missing or outside ``[0, num_blocks)`` for the lengths
+    ``seq_lens [B] int32``; returns a device ``int32 [1]`` tensor (0: valid)."""
+    B = seq_lens.shape[0]
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.stride(1) == 1
+    if max_vblocks is None:
+        max_vblocks = block_table.shape[1]
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=seq_lens.device)
+    _check("dcp_check_block_table", lib().dcp_check_block_table(
+        _ptr(block_table), B, block_table.stride(0), max_vblocks, _ptr(seq_lens), block_size, dcp_size, num_blocks,
+        _ptr(out), _stream(stream)))
     return out
 
 

@@ -231,3 +231,17 @@ def test_gather_validation(L):
     assert call(out_v=p) == UNS                            # V transposed inside a block
     assert call(kv=_kv(head_dim_k=4)) == UNS               # rows under 16 bytes
     assert call(total=0, cu=NULL, out_k=NULL) == 0         # nothing to gather
+
+
+def test_check_block_table_validation(L):
+    p = _fake()
+    call = L.dcp_check_block_table
+    assert call(p, 2, 8, 8, p, 0, 4, 10, p, NULL) == INV       # block_size
+    assert call(p, 2, 8, 8, p, 16, 0, 10, p, NULL) == INV      # dcp_size
+    assert call(p, -1, 8, 8, p, 16, 4, 10, p, NULL) == INV     # num_reqs
+    assert call(p, 2, 4, 8, p, 16, 4, 10, p, NULL) == INV      # stride below max_vblocks
+    assert call(p, 2, 8, -1, p, 16, 4, 10, p, NULL) == INV     # max_vblocks
+    assert call(p, 2, 8, 8, p, 16, 4, -1, p, NULL) == INV      # num_blocks
+    assert call(p, 2, 8, 8, p, 16, 4, 10, NULL, NULL) == INV   # bad_count
+    assert call(p, 2, 8, 8, NULL, 16, 4, 10, p, NULL) == INV   # seq_lens
+    assert call(NULL, 2, 8, 8, p, 16, 4, 10, p, NULL) == INV   # block table
