@@ -58,8 +58,10 @@ SEGMENT_METRIC = "decode with a replicated segment: KV GB/s (% of MI355X HBM pea
 GATHER_METRIC = "context gather GB/s (stored rows read + written) at 1 GPU"
 KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
                 "kv_write": "kv_write", "gather": "gather_context_kernel"}
-KERNEL_SOURCES = {"gqa": "attn_gqa.hip", "mla": "attn_mla.hip", "generic": "attn_generic.hip",
-                  "kv_write": "kv_write.hip", "gather": "gather.hip"}
+# Sources compiled into each kernel family (the attention kernels include the
+# split-KV header, which fixes their workspace layout).
+KERNEL_SOURCES = {"gqa": ["attn_gqa.hip", "splitkv.h"], "mla": ["attn_mla.hip", "splitkv.h"],
+                  "generic": ["attn_generic.hip"], "kv_write": ["kv_write.hip"], "gather": ["gather.hip"]}
 
 
 def kernel_family(w):
@@ -71,9 +73,12 @@ def kernel_family(w):
 
 
 def source_hash(family):
-    path = os.path.join(ROOT, "sequence_sharded_paged_amd", "csrc", KERNEL_SOURCES[family])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the family's sources, concatenated in the listed order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "sequence_sharded_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(family, workload):

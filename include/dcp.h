@@ -353,7 +353,7 @@ int dcp_partial_segment_attn(const void* q, int32_t q_dtype, int32_t batch, int3
  *
  * part_o    device, [num_parts, batch, num_heads, head_dim_v] float32
  * part_lse  device, [num_parts, batch, num_heads] float32
- * num_parts 1..64; batch >= 0; num_heads >= 1; head_dim_v 1..1024
+ * num_parts 1..64; batch >= 0; num_heads >= 1; head_dim_v 1..4096
  * sink      device, [num_heads] float32, or NULL
  * out_dtype DCP_F32 or DCP_BF16 (round to nearest even)
  * out_o     device, [batch, num_heads, head_dim_v]

@@ -74,20 +74,33 @@ def test_slot_mapping_max_vblocks_bound(device):
 # ---------------------------------------------------------------------------
 # LSE merge
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("R,with_sink,out", [(1, False, torch.float32), (2, True, torch.float32),
-                                              (8, True, torch.bfloat16), (8, False, torch.bfloat16),
-                                              (5, True, torch.float32), (64, False, torch.float32)])
-def test_lse_merge(device, R, with_sink, out):
-    rng = np.random.default_rng(R * 10 + with_sink)
-    B, H, Dv = 3, 16, 72
+@pytest.mark.parametrize("R,with_sink,out,B,H,Dv,offset", [
+    (1, False, torch.float32, 3, 16, 72, 0), (2, True, torch.float32, 3, 16, 72, 0),
+    (8, True, torch.bfloat16, 3, 16, 72, 0), (8, False, torch.bfloat16, 3, 16, 72, 0),
+    (5, True, torch.float32, 3, 16, 72, 0), (64, False, torch.float32, 3, 16, 72, 0),
+    # odd width (one value per thread), a width past one block of threads, and
+    # rows that start off the 16-byte boundary (output and parts): scalar path
+    (3, True, torch.bfloat16, 2, 5, 37, 0), (9, True, torch.float32, 2, 3, 1100, 0),
+    (8, True, torch.float32, 2, 7, 128, 1), (8, False, torch.bfloat16, 2, 7, 128, 1),
+    # the decode workloads' widths over many rows; more parts than one load batch
+    (8, True, torch.bfloat16, 40, 64, 128, 0), (8, True, torch.bfloat16, 5, 128, 512, 0),
+    (17, False, torch.float32, 6, 32, 512, 0), (12, True, torch.float32, 4, 3, 4, 0),
+])
+def test_lse_merge(device, R, with_sink, out, B, H, Dv, offset):
+    rng = np.random.default_rng(R * 10 + with_sink + Dv)
     po = rng.standard_normal((R, B, H, Dv)).astype(np.float32)
     pl = (rng.standard_normal((R, B, H)) * 4).astype(np.float32)
     pl[rng.random((R, B, H)) < 0.3] = -np.inf                 # empty shards
     pl[:, 0, 0] = -np.inf                                      # an all-empty head
     po[np.isneginf(pl)] = 0.0
     sink = (rng.standard_normal(H) + 1).astype(np.float32) if with_sink else None
-    o, lse = dcp.dcp_lse_merge(torch.from_numpy(po).to(device), torch.from_numpy(pl).to(device),
-                               sink=None if sink is None else torch.from_numpy(sink).to(device), out_dtype=out)
+    # offset = 1: the part and output buffers start one element into an allocation
+    po_dev = torch.empty(po.size + offset, dtype=torch.float32, device=device)[offset:].view(R, B, H, Dv)
+    po_dev.copy_(torch.from_numpy(po))
+    out_dev = torch.full(((B * H * Dv) + offset,), float("nan"), dtype=out, device=device)[offset:].view(B, H, Dv)
+    o, lse = dcp.dcp_lse_merge(po_dev, torch.from_numpy(pl).to(device),
+                               sink=None if sink is None else torch.from_numpy(sink).to(device), out_dtype=out,
+                               out_o=out_dev)
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     for b in range(B):
         ro, rl = oatt.lse_merge(po[:, b], pl[:, b], sink)
