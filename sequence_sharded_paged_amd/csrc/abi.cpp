@@ -10,13 +10,10 @@
 
 namespace dcp {
 
+// CU count of the current device, cached per device (static storage starts
+// zeroed; concurrent first calls store the same value).
 int device_cu_count() {
   static std::atomic<int> cache[64];
-  static std::atomic<bool> init{false};
-  if (!init.load()) {
-    for (auto& c : cache) c.store(0);
-    init.store(true);
-  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
   if (dev < 64 && cache[dev].load() > 0) return cache[dev].load();

@@ -30,6 +30,8 @@
 // product: no LDS, no shuffles besides the max/sum reductions. fp8 codes are
 // widened to bf16 in registers (exact) and the per-head scales are applied to
 // the scores and to the output, outside the dot products.
+#include <atomic>
+
 #include "splitkv.h"
 
 namespace dcp {
@@ -411,17 +413,20 @@ size_t gqa_workspace_bytes(const AttnParams& p) {
   return split_ws_bytes(split_units_host(p), kGqaMaxWorkers, p.tpu * p.group, kGqaDim);
 }
 
+// Persistent wavefronts the device holds at once, cached per device (static
+// storage starts zeroed; concurrent first calls store the same value).
 template <bool kFp8>
 static int gqa_workers() {
-  static int cached[2] = {0, 0};
-  int& c = cached[kFp8 ? 1 : 0];
-  if (c == 0) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_attn_kernel<kFp8>, 64 * kGqaWavesPerBlock, 0) !=
-            hipSuccess || per_cu < 1)
-      per_cu = 2;
-    c = min(kGqaMaxWorkers, device_cu_count() * per_cu * kGqaWavesPerBlock);
-  }
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cached[dev].load() > 0) return cached[dev].load();
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gqa_attn_kernel<kFp8>, 64 * kGqaWavesPerBlock, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 2;
+  const int c = min(kGqaMaxWorkers, device_cu_count() * per_cu * kGqaWavesPerBlock);
+  if (dev < 64) cached[dev].store(c);
   return c;
 }
 
