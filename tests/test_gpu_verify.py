@@ -95,3 +95,19 @@ def test_verify_matches_across_kernels(device):
     fin = torch.isfinite(b[1])
     assert torch.equal(torch.isfinite(a[1]), fin)
     assert (a[1][fin] - b[1][fin]).abs().max().item() <= 1e-3
+
+
+def test_verify_many_pairs_per_planner_thread(device):
+    """More (rank, request) pairs than planner threads (200 requests x 8 ranks
+    > 1024) with two token groups per pair (q_len = 3 > 16 / group) and 8 KV
+    heads: every unit's tile prefix comes from the planner's pair walk. Short
+    ragged lengths keep the oracle cheap; every request is checked."""
+    w = get_workload("gqa_fp8_binned")
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(3, 400, size=200)]
+    case = make_case(w, device=device, seq_lens=lens)
+    inp = DeviceInputs(case, device)
+    q = make_verify_queries(w, case.batch, 3, device)
+    for algo in (FAST, GEN):
+        run = VerifyRun(inp, q, algo=algo)
+        check_verify_against_oracle(run, run.run())
