@@ -144,7 +144,10 @@ def kv_write_kernels(w):
     """The kernels one dcp_kv_cache_write call launches for this workload."""
     if w.tokens < 1024:
         return ["kv_scatter_kernel"]
-    return ["kv_rows_kernel"] + ([] if w.geometry().mla else ["kv_vt16_kernel"])
+    g = w.geometry()
+    if g.mla:
+        return ["kv_rows_kernel"]  # 576-wide latent rows: 36 pieces of 16, the general row kernel
+    return ["kv_tokrow_kernel", "kv_vt16_kernel"]  # 8 x 128 K rows; V stored dim-major
 
 
 def cpu_baseline_kv_write(case, budget_s):

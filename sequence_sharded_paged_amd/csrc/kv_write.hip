@@ -6,13 +6,16 @@
 // note), section "Cache ownership" (a write turns the virtual slot into the
 // owner's local slot; non-owners are masked).
 //
-// Three kernels, chosen by batch size and V layout (see each):
+// Kernels, chosen by batch size, row width and V layout (see each):
 //   * kv_scatter_kernel, batches under 1024 tokens (a decode step): one
 //     wavefront per (token, KV head), shortest chain of memory accesses;
-//   * kv_rows_kernel, larger batches, K rows (and V rows in a row layout):
-//     one wavefront per few tokens (all KV heads), owners found by a ballot
-//     over (token, rank) lanes, whole rows loaded and stored with 8-element
-//     chunks;
+//   * kv_tokrow_kernel, larger batches whose token rows are 48 .. 64 pieces
+//     of 16 elements (GQA K, and V in a row layout): a wavefront per run of
+//     tokens, one token at a time across its lanes, 16-byte stores;
+//   * kv_rows_kernel, larger batches, other rows (MLA's 576-wide latent,
+//     unaligned pools): one wavefront per few tokens (all KV heads), owners
+//     found by a ballot over (token, rank) lanes, whole rows loaded and
+//     stored with 8-element chunks;
 //   * kv_vt_kernel, larger batches, V stored token-contiguous inside a block
 //     (the layout the attention kernel reads): 64-token tiles transposed
 //     through LDS so that consecutive slots of a block are stored together.
@@ -152,6 +155,27 @@ __device__ __forceinline__ void store8(void* pool, int64_t elem, int64_t dim_str
   }
 }
 
+// Sixteen stored values at a 16-byte aligned, contiguous destination.
+template <int kDst>
+__device__ __forceinline__ void store16(void* pool, int64_t elem, const uint32_t (&q)[16]) {
+  using St = typename Stored<kDst>::T;
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<St*>(pool) + elem);
+  if constexpr (kDst == DCP_FP8_E4M3) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = q[4 * i] | (q[4 * i + 1] << 8) | (q[4 * i + 2] << 16) | (q[4 * i + 3] << 24);
+    dst[0] = uint4{w[0], w[1], w[2], w[3]};
+  } else if constexpr (kDst == DCP_BF16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dst[i] = uint4{q[8 * i] | (q[8 * i + 1] << 16), q[8 * i + 2] | (q[8 * i + 3] << 16),
+                     q[8 * i + 4] | (q[8 * i + 5] << 16), q[8 * i + 6] | (q[8 * i + 7] << 16)};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = uint4{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
+  }
+}
+
 struct KvWriteParams {
   const void* k_new;
   const void* v_new;     // nullptr: no V rows (MLA)
@@ -177,6 +201,7 @@ struct RowsArgs {
   int tpw;               // tokens per wavefront (a power of two, tpw * rank_lanes <= 64)
   uint32_t tok_magic;    // c / (H * dim / 8) = umulhi(c, tok_magic) for the chunk numbers c used here
   uint32_t head_magic;   // c / (dim / 8) = umulhi(c, head_magic)
+  int bs_shift;          // kv_tokrow_kernel: log2(block_size), or -1 when it is not a power of two
 };
 
 constexpr int kRowsRounds = 9;  // 64-chunk rounds of a wavefront's rows held in registers
@@ -777,6 +802,67 @@ __global__ void __launch_bounds__(256) kv_scatter_kernel(KvWriteParams p) {
   }
 }
 
+// Large batches, rows of 48 .. 64 pieces of 16 elements (GQA: 8 KV heads x
+// 128 dims = 64 pieces): a wavefront walks its tokens one at a time, lane l
+// taking elements 16 l .. 16 l + 15 of the token's row. The owner's row
+// address is then wave-uniform (one slot read per rank, no shuffles), a
+// lane's head and fp8 scale are fixed for the whole launch, and every lane
+// stores its 16 values at once. kTokUnroll tokens' sources and slots are
+// loaded before the first is converted.
+constexpr int kTokUnroll = 4;
+
+template <int kDst, bool kSrcBf16>
+__global__ void __launch_bounds__(256) kv_tokrow_kernel(KvWriteParams p, RowsArgs a, int tok_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int64_t T = p.num_tokens;
+  const int64_t t_begin = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * tok_per_wave;
+  if (t_begin >= T) return;  // whole wavefronts leave together
+  const int64_t t_end = T - t_begin < tok_per_wave ? T : t_begin + tok_per_wave;
+  const int H = p.kv.num_kv_heads, dim = a.dim, bs = p.kv.block_size;
+  const int pieces = H * dim / 16;
+  const bool act = lane < pieces;
+  const int e0 = 16 * (act ? lane : pieces - 1);  // idle lanes load a valid piece and store nothing
+  const int h = e0 / dim, d0 = e0 - h * dim;
+  const int64_t row_elems = static_cast<int64_t>(H) * dim;
+  const int64_t cap = static_cast<int64_t>(p.kv.num_blocks) * bs;
+  const int64_t lane_off = h * a.st[2] + d0;  // dim stride 1 (checked on the host)
+  double rcp = 1.0;
+  if constexpr (kDst == DCP_FP8_E4M3) rcp = scale_rcp(a.scale, h);
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTokUnroll) {
+    Raw8<kSrcBf16> raw[kTokUnroll][2];
+    int64_t slot[kTokUnroll];
+#pragma unroll
+    for (int j = 0; j < kTokUnroll; ++j) {
+      const int64_t t = t0 + j < t_end ? t0 + j : t_end - 1;  // in range; repeats are skipped below
+      slot[j] = lane < p.num_ranks ? p.slots[lane * T + t] : -1;
+      raw[j][0] = load8<kSrcBf16>(a.src, t * row_elems + e0);
+      raw[j][1] = load8<kSrcBf16>(a.src, t * row_elems + e0 + 8);
+    }
+#pragma unroll
+    for (int j = 0; j < kTokUnroll; ++j) {
+      if (t0 + j >= t_end) break;  // wave-uniform
+      uint32_t q[16];
+      uint32_t (&lo)[8] = *reinterpret_cast<uint32_t(*)[8]>(&q[0]);
+      uint32_t (&hi)[8] = *reinterpret_cast<uint32_t(*)[8]>(&q[8]);
+      convert8<kDst, kSrcBf16>(raw[j][0], rcp, lo);
+      convert8<kDst, kSrcBf16>(raw[j][1], rcp, hi);
+      uint64_t owners = __builtin_amdgcn_ballot_w64(slot[j] >= 0 && slot[j] < cap);
+      while (owners) {  // wave-uniform: normally one owner
+        const int r = __builtin_ctzll(owners);
+        owners &= owners - 1;
+        const uint32_t s_lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(slot[j]), r);
+        const uint32_t s_hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(static_cast<uint64_t>(slot[j]) >> 32), r);
+        const int64_t s = static_cast<int64_t>((static_cast<uint64_t>(s_hi) << 32) | s_lo);
+        const int64_t blk = a.bs_shift >= 0 ? (s >> a.bs_shift) : s / bs;
+        const int64_t off = s - blk * bs;
+        const int64_t row = r * a.st[0] + blk * a.st[1] + off * a.st[3];
+        if (act) store16<kDst>(a.pool, row + lane_off, q);
+      }
+    }
+  }
+}
+
 // Whether every chunk of 8 elements of a pool is contiguous and aligned for a
 // vector store of 8 elements (16 bytes for 2- and 4-byte elements, 8 for fp8).
 static int chunks_vectorizable(const void* base, const int64_t* st, int elem_bytes) {
@@ -785,6 +871,20 @@ static int chunks_vectorizable(const void* base, const int64_t* st, int elem_byt
     if (st[i] % 8 != 0) return 0;
   const uintptr_t align = elem_bytes == 1 ? 8 : 16;
   return reinterpret_cast<uintptr_t>(base) % align == 0;
+}
+
+// kv_tokrow_kernel applies when a token's row is 48 .. 64 pieces of 16
+// elements that never straddle a head, every piece of the pool is contiguous
+// and 16-byte aligned, the source rows are 16-byte aligned and every rank's
+// slot has a lane.
+static bool tokrow_fits(const KvWriteParams& p, const RowsArgs& a, int64_t pieces) {
+  const int eb = p.kv.dtype == DCP_F32 ? 4 : p.kv.dtype == DCP_BF16 ? 2 : 1;
+  if (a.dim % 16 != 0 || pieces < 48 || pieces > 64 || p.num_ranks > 64) return false;
+  if (a.st[4] != 1 || reinterpret_cast<uintptr_t>(a.pool) % 16 != 0 || reinterpret_cast<uintptr_t>(a.src) % 16 != 0)
+    return false;
+  for (int i = 0; i < 4; ++i)
+    if ((a.st[i] * eb) % 16 != 0) return false;
+  return true;
 }
 
 // Batches below this many tokens take the one-wavefront-per-(token, head)
@@ -813,6 +913,20 @@ static void launch_typed(const KvWriteParams& p, hipStream_t stream) {
     while (a.tpw > 1 && static_cast<uint64_t>(a.tpw) * cptok > 64 * kRowsRounds) a.tpw /= 2;
     a.tok_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + cptok - 1) / cptok);
     a.head_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + cpt - 1) / cpt);
+    a.bs_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == p.kv.block_size) a.bs_shift = sh;
+    const int64_t pieces = H * dim / 16;
+    if (tokrow_fits(p, a, pieces)) {
+      // about eight wavefronts per SIMD, each a multiple of kTokUnroll tokens
+      const int64_t target = static_cast<int64_t>(device_cu_count()) * 32;
+      int64_t tpw = (T + target - 1) / target;
+      tpw = (tpw + kTokUnroll - 1) / kTokUnroll * kTokUnroll;
+      const int64_t waves = (T + tpw - 1) / tpw;
+      hipLaunchKernelGGL((kv_tokrow_kernel<kDst, kSrcBf16>), dim3(static_cast<unsigned>((waves + 3) / 4)),
+                         dim3(256), 0, stream, p, a, static_cast<int>(tpw));
+      return;
+    }
     const int64_t waves = (T + a.tpw - 1) / a.tpw;
     hipLaunchKernelGGL((kv_rows_kernel<kDst, kSrcBf16>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
                        0, stream, p, a);

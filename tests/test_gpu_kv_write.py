@@ -131,8 +131,12 @@ def _slots_for(rng, T, R, N, bs, I):
     return slots
 
 
-# Batches under 1024 tokens take the per-(token, head) kernel, larger ones the
-# 64-token tile kernel (whose last tile is ragged in the cases below).
+# Batches under 1024 tokens take the per-(token, head) kernel. Larger ones take
+# the one-token-per-wavefront row kernel when a token's row is 48..64 pieces
+# of 16 elements in aligned pools (the last two cases: 8 x 128 with a block
+# size that is not a power of two, 3 x 256 with 16 idle lanes; padded pools
+# fall back), else the general row kernel; V stored dim-major takes the
+# 64-token tile kernels (whose last tile is ragged in the cases below).
 GQA_CASES = [
     # (H, Dk, Dv, bs, R, I, N, T)
     (2, 16, 16, 16, 4, 1, 6, 70),
@@ -141,6 +145,8 @@ GQA_CASES = [
     (1, 8, 8, 1, 2, 1, 40, 33),
     (2, 16, 16, 16, 4, 1, 80, 1100),
     (3, 24, 136, 8, 3, 8, 150, 1030),
+    (8, 128, 128, 24, 4, 8, 40, 1301),
+    (3, 256, 256, 16, 3, 16, 60, 1030),
 ]
 
 
