@@ -225,7 +225,9 @@ size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads
  * workspace   device, >= the size query's bytes (may be NULL if that is 0)
  * Errors: DCP_ERR_INVALID_ARG (sizes, relations, NULL pointers,
  * num_q_heads % num_kv_heads != 0, head_dim_v > head_dim_k with v == NULL,
- * fp8 without scales), DCP_ERR_UNSUPPORTED, DCP_ERR_WORKSPACE, DCP_ERR_HIP.
+ * fp8 without scales), DCP_ERR_UNSUPPORTED (also when rank_count * batch *
+ * num_kv_heads split units, or rank_count * batch * num_q_heads rows for the
+ * generic kernel, exceed 2^31 - 1), DCP_ERR_WORKSPACE, DCP_ERR_HIP.
  */
 int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                             const dcp_kv_cache_t* kv, const int32_t* block_table,

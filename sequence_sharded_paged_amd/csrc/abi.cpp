@@ -1,6 +1,7 @@
 // C ABI entry points of libdcp: host-side validation, kernel selection and
 // launch. The operations and their sources are documented in include/dcp.h.
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <cmath>
 #include <utility>
@@ -62,21 +63,31 @@ static int validate_attn(int32_t batch, int32_t q_len, int32_t num_q_heads, int3
     p.tpu = tpu;
     p.ntg = (q_len + tpu - 1) / tpu;
   };
+  // The MFMA kernels' split plan names units (rank, request, KV head, token
+  // group) with 32-bit indices.
+  auto units_fit = [&]() {
+    return static_cast<int64_t>(rank_count) * batch * kv->num_kv_heads * p.ntg <= INT32_MAX;
+  };
   tokens_per_unit(std::max(1, std::min(q_len, 16 / std::max(1, p.group))));
-  if (algo != DCP_ALGO_GENERIC && gqa_supported(p)) {
+  if (algo != DCP_ALGO_GENERIC && units_fit() && gqa_supported(p)) {
     kernel = AttnKernel::GqaMfma;
     return DCP_OK;
   }
   tokens_per_unit(1);
   if (algo == DCP_ALGO_GENERIC) {
     kernel = AttnKernel::Generic;
-  } else if (mla_supported(p)) {
+  } else if (units_fit() && mla_supported(p)) {
     kernel = AttnKernel::MlaMfma;
   } else if (algo == DCP_ALGO_FAST) {
     return DCP_ERR_UNSUPPORTED;
   } else {
     kernel = AttnKernel::Generic;
   }
+  // the generic kernel runs one workgroup per (rank, request, query token,
+  // query head), indexed in 32 bits
+  if (kernel == AttnKernel::Generic &&
+      static_cast<int64_t>(rank_count) * batch * q_len * num_q_heads > INT32_MAX)
+    return DCP_ERR_UNSUPPORTED;
   return DCP_OK;
 }
 

@@ -111,6 +111,15 @@ def test_workspace_size_is_host_only(L):
     assert st == INV
     st, _ = _ws(L, _kv(head_dim_k=64, head_dim_v=64), algo=native.DCP_ALGO_FAST)
     assert st == UNS                              # no MFMA kernel for d=64
+    # more split units (rank x request x KV head) than 32-bit indices hold: no
+    # MFMA kernel, and the generic kernel's workgroups (rank x request x query
+    # head, never fewer) do not fit either
+    st, n = _ws(L, _kv(), batch=1 << 27, rc=16, hq=2, algo=native.DCP_ALGO_FAST)
+    assert st == UNS
+    st, n = _ws(L, _kv(), batch=1 << 27, rc=16, hq=2)
+    assert st == UNS and n == 0
+    st, n = _ws(L, _kv(), batch=1 << 25, rc=16, hq=2)  # 2^30 units: the MFMA plan
+    assert st == 0 and n > 0
 
 
 def test_partial_attn_validation(L):
