@@ -248,3 +248,24 @@ def test_moderate_needles(device, name):
     inp = DeviceInputs(case, device)
     for algo in _algos(name):
         check_against_oracle(inp, inp.run(algo=algo))
+
+
+@pytest.mark.parametrize("name,lens", [("gqa_fp8_binned", [3000, 129, 7000, 1]),
+                                       ("gqa_bf16_32k", [900, 2100, 5]),
+                                       ("mla_bf16_bimodal", [3000, 650, 9000])])
+def test_partials_into_unaligned_outputs(device, name, lens):
+    """out_o and out_lse one float into their allocations (off the 16-byte
+    grid): the MFMA kernels and the split combine (element-wise stores there)
+    write the same partials, bit for bit, as into aligned outputs."""
+    w = get_workload(name)
+    inp = DeviceInputs(make_case(w, device=device, seq_lens=lens), device).prepare(algo=dcp.DCP_ALGO_FAST)
+    inp.partial()
+    torch.cuda.synchronize()
+    ref_o, ref_l = inp.po.clone(), inp.pl.clone()
+    po = torch.full((inp.po.numel() + 1,), float("nan"), device=device)[1:].view(inp.po.shape)
+    pl = torch.full((inp.pl.numel() + 1,), float("nan"), device=device)[1:].view(inp.pl.shape)
+    dcp.dcp_partial_decode_attn(inp.q, inp.kv, inp.block_table, inp.local_lens, inp.D, inp.rank_begin,
+                                inp.rank_count, w.softmax_scale, po, pl, inp.ws, algo=dcp.DCP_ALGO_FAST)
+    torch.cuda.synchronize()
+    assert po.data_ptr() % 16 != 0
+    assert torch.equal(po, ref_o) and torch.equal(pl, ref_l)
