@@ -8,10 +8,15 @@ import numpy as np
 import torch
 
 import sequence_sharded_paged_amd as dcp
-from oracle import attention as oatt
-from oracle import formats as ofmt
-from oracle import layout as olay
 from workloads.generate import stored_numpy, stored_format
+
+
+def _oracle():
+    """The oracle modules, imported only by the functions that check against
+    them: the device-side set-up below (DeviceInputs, VerifyRun,
+    SegmentInputs), which bench.py also uses, never loads the oracle."""
+    from oracle import attention, formats, layout
+    return attention, formats, layout
 
 TOL = {
     "fp32": dict(max_abs=1e-5, row_rel=1e-4, lse=1e-5),
@@ -107,6 +112,7 @@ class DeviceInputs:
 def oracle_request(case, b, dcp_size=None, interleave=None, with_partials=True):
     """Float64 oracle for request b: full attention (with the sink) and the
     per-rank partials over the brute-force ownership."""
+    oatt, ofmt, olay = _oracle()
     w = case.workload
     D = dcp_size or w.dcp_size
     I = interleave or w.interleave
@@ -224,6 +230,7 @@ class VerifyRun:
 def oracle_verify_request(case, q, b, dcp_size, interleave):
     """Float64 oracle for request b's q_len query tokens: causal attention over
     the cached sequence (with the sink) and the per-rank partials."""
+    oatt, ofmt, olay = _oracle()
     w = case.workload
     qb = ofmt.decode(stored_numpy(q[b]), stored_format(q))                     # [q_len, Hq, Dk]
     k = ofmt.decode_kv(stored_numpy(case.k[b]), stored_format(case.k[b]), case.k_scale)
@@ -294,6 +301,7 @@ def oracle_segment_request(case, seg, b, dcp_size, interleave, seg_rank):
     """Float64 oracle for request b with its segment: attention over the
     sequence and the segment together (sink included) and the per-rank
     partials with the segment on rank seg_rank."""
+    oatt, ofmt, olay = _oracle()
     w = case.workload
     q = ofmt.decode(stored_numpy(case.q[b]), stored_format(case.q))
 

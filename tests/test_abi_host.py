@@ -254,3 +254,17 @@ def test_check_block_table_validation(L):
     assert call(p, 2, 8, 8, p, 16, 4, 10, NULL, NULL) == INV   # bad_count
     assert call(p, 2, 8, 8, NULL, 16, 4, 10, p, NULL) == INV   # seq_lens
     assert call(NULL, 2, 8, 8, p, 16, 4, 10, p, NULL) == INV   # block table
+
+
+def test_product_path_loads_no_oracle():
+    """The package, the workload generators and the device-side set-up that
+    bench.py times through load no module of the oracle (it enters only in
+    the tests' checks and bench.py's cpu_baseline functions)."""
+    import subprocess
+    import sys
+    code = ("import sys; import sequence_sharded_paged_amd, workloads, workloads.generate, tests.harness; "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
