@@ -15,7 +15,13 @@ distributions of the named workload). Prints ONE JSON line:
                 rocprofv3 counter summary when it was taken on the current
                 kernel source, else null;
 * ``cpu_baseline`` - the float64 CPU oracle timed on a bounded sample of the
-                same batch (rank 0, N = 1 only).
+                same batch (rank 0, N = 1 only);
+* ``per_config``- (default run) the same measurements for the GQA bf16, the
+                two MLA and the GQA fp8 decode workloads, each with a shorter
+                oracle sample, the MLA ones also against the bf16 MFMA peak;
+* ``layout``  - local lengths and the slot mapping (one decode step's new
+                tokens, and the bulk fill of every cached token) timed apart
+                from the step, with the oracle's brute-force mapper beside it.
 
 With a multi-token decode workload (``--workload *_q<N>``) a step is every
 rank's partial attention for the last N tokens of every request at once
@@ -333,7 +339,7 @@ def bench_verify(args, vw):
     import numpy as np
     import torch
     import sequence_sharded_paged_amd as dcp
-    from tests.harness import DeviceInputs, VerifyRun
+    from workloads.device import DeviceInputs, VerifyRun
     from workloads import make_case, make_verify_queries
 
     w = vw.geometry()
@@ -375,7 +381,7 @@ def bench_verify(args, vw):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_DESC[w.kv_format],
         "data": "synthetic",
         "config": {
             "workload": vw.name,
@@ -413,7 +419,7 @@ def bench_segment(args, sw):
     import numpy as np
     import torch
     import sequence_sharded_paged_amd as dcp
-    from tests.harness import DeviceInputs, SegmentInputs
+    from workloads.device import DeviceInputs, SegmentInputs
     from workloads import make_case, make_segment
 
     w = sw.geometry()
@@ -470,7 +476,7 @@ def bench_segment(args, sw):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_DESC[w.kv_format],
         "data": "synthetic",
         "config": {
             "workload": sw.name,
@@ -544,7 +550,7 @@ def bench_gather(args, name):
     import numpy as np
     import torch
     import sequence_sharded_paged_amd as dcp
-    from tests.harness import DeviceInputs
+    from workloads.device import DeviceInputs
     from workloads import get_workload, make_case
 
     w = get_workload(name[len("gather_"):])
@@ -589,7 +595,7 @@ def bench_gather(args, name):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": f"{w.kv_format} (stored bits copied)",
         "data": "synthetic",
         "config": {"workload": name, "base": w.name, "requests": case.batch, "tokens": T,
                    "bytes_per_token": 2 * w.kv_bytes_per_token(), "kernel": "gather_context_kernel",
@@ -627,14 +633,224 @@ def cpu_baseline_gather(inp, case, budget_s):
             "sample": f"{len(done)} of {case.batch} requests gathered one at a time by the oracle; {spent:.1f} s"}
 
 
+DTYPE_DESC = {
+    "fp32": "f32 KV, fp32 arithmetic",
+    "bf16": "bf16 KV, bf16 MFMA, fp32 accumulate",
+    "fp8_e4m3": "fp8_e4m3 KV (widened exactly to bf16 MFMA operands, per-head scales), fp32 accumulate",
+}
+PER_CONFIG = ["gqa_bf16_32k", "mla_bf16_bimodal", "mla_bf16_longtail_sink", "gqa_fp8_binned"]
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def host_cores():
+    """Host cores this process may run on, and the BLAS thread count."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return aff, blas_threads()
+
+
+def load_counters(family, workload):
+    """MFMA-busy and fetched-bytes figures from the committed counter summary
+    of this kernel and workload, if it was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[family]}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(family):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "lds_bank_conflict_cycles", "source_sha256_16") if k in rec}
+
+
+def step_flops(w, tokens):
+    """Algorithmic matrix flops of one decode step: QK^T and PV over every
+    cached token, for every query head."""
+    return 2 * tokens * w.num_q_heads * (w.head_dim_k + w.head_dim_v)
+
+
+def step_bytes(w, case, out_elem):
+    """Algorithmic HBM bytes of one decode step: the KV once, every rank's
+    read of the queries, the rank partials written and read back (O and LSE,
+    float32) and the merged output (O and LSE)."""
+    B, Hq, Dk, Dv, D = case.batch, w.num_q_heads, w.head_dim_k, w.head_dim_v, w.dcp_size
+    q_elem = 4 if w.q_format == "fp32" else 2
+    kv = case.kv_bytes()
+    q = D * B * Hq * Dk * q_elem
+    parts = 2 * D * B * Hq * (Dv + 1) * 4
+    final = B * Hq * (Dv * out_elem + 4)
+    return {"kv": int(kv), "q_reads": int(q), "partials_write_read": int(parts), "final_out": int(final),
+            "total": int(kv + q + parts + final)}
+
+
+def measure_decode(w, steps, warmup, cpu_budget_s):
+    """One decode workload: inputs resident in HBM, `steps` timed decode steps
+    (all ranks' partials + merge), the attention kernel timed alone with the
+    library's HIP events on its stream, and the oracle on a bounded sample."""
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from workloads import make_case
+    from workloads.device import DeviceInputs
+
+    t_gen = time.perf_counter()
+    case = make_case(w, device="cuda")
+    inp = DeviceInputs(case, "cuda", fill="zero")
+    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name}: batch {case.batch}, {int(case.seq_lens.sum())} tokens, "
+          f"{case.kv_bytes() / 1e9:.3f} GB KV, inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        inp.step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dcp.native.dcp_profile_enable(True)
+    dcp.native.dcp_profile_collect()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        inp.step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern_ms, launches = dcp.native.dcp_profile_collect()
+    dcp.native.dcp_profile_enable(False)
+    ms = start.elapsed_time(stop) / steps
+    kern_avg_ms = kern_ms / max(launches, 1)
+    tokens = int(case.seq_lens.astype(np.int64).sum())
+    kv_bytes = case.kv_bytes()
+    family = kernel_family(w)
+    out_elem = 2 if w.out_format == "bf16" else 4
+    ab = step_bytes(w, case, out_elem)
+    flops = step_flops(w, tokens)
+    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(family, w.name)
+    res = {
+        "workload": w.name,
+        "batch": case.batch,
+        "tokens": tokens,
+        "kv_format": w.kv_format,
+        "dtype": DTYPE_DESC[w.kv_format],
+        "kernel": KERNEL_NAMES[family],
+        "ms_per_step": round(ms, 5),
+        "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "pct_hbm_peak": round(100.0 * kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "merged_queries_per_s": round(case.batch / (ms * 1e-3), 1),
+        "algorithmic_bytes": ab,
+        "algorithmic_total_gbs": round(ab["total"] / (ms * 1e-3) / 1e9, 2),
+        "step_overhead_ms": round(ms - kern_avg_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "fetch_gbs": None if traffic is None else round(traffic / (kern_avg_ms * 1e-3) / 1e9, 2),
+            "kernel_avg_ms": round(kern_avg_ms, 5),
+            "mfma_tflops": round(flops / (kern_avg_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (kern_avg_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "counters": load_counters(family, w.name),
+        },
+        "cpu_baseline": None,
+    }
+    if cpu_budget_s > 0:
+        cb = cpu_baseline(case, cpu_budget_s)
+        cb["speedup_gpu_over_oracle"] = round(res["kv_gbs"] / cb["value"], 1)
+        res["cpu_baseline"] = cb
+    del inp, case
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_layout(w, steps, cpu_budget_s):
+    """The layout steps of the path on one workload's batch, timed apart from
+    the decode step: local lengths and the slot mapping of one decode step's
+    new tokens (one per request), and the slot mapping of the bulk fill (every
+    cached token); the oracle's brute-force mapper on a sample of the same
+    tokens."""
+    import numpy as np
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    from workloads.generate import make_block_table, sample_lengths
+
+    lens = sample_lengths(w)
+    table, _ = make_block_table(w, lens, extra_vblocks=1)
+    dev = "cuda"
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    bt = torch.from_numpy(table).to(dev)
+    B, D = len(lens), w.dcp_size
+    local = torch.empty((B, D), dtype=torch.int32, device=dev)
+    dec_pos = torch.from_numpy(lens.astype(np.int64)).to(dev)            # the next token of every request
+    dec_req = torch.arange(B, dtype=torch.int32, device=dev)
+    dec_slots = torch.empty((D, B), dtype=torch.int64, device=dev)
+    T = int(lens.astype(np.int64).sum())
+    bulk_pos = torch.cat([torch.arange(int(L), dtype=torch.int64, device=dev) for L in lens])
+    bulk_req = torch.repeat_interleave(torch.arange(B, dtype=torch.int32, device=dev),
+                                       torch.from_numpy(lens.astype(np.int64)).to(dev))
+    bulk_slots = torch.empty((D, T), dtype=torch.int64, device=dev)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_local = timed(lambda: dcp.dcp_local_seq_lens(seq, w.block_size, D, w.interleave, out=local), steps)
+    ms_dec = timed(lambda: dcp.dcp_slot_mapping(dec_pos, dec_req, bt, w.block_size, D, w.interleave,
+                                                out=dec_slots), steps)
+    ms_bulk = timed(lambda: dcp.dcp_slot_mapping(bulk_pos, bulk_req, bt, w.block_size, D, w.interleave,
+                                                 out=bulk_slots), max(1, steps // 4))
+    bulk_bytes = T * (8 + 4) + D * T * 8 + T * 4   # positions + request ids read, slots written, table entries
+    res = {
+        "workload": w.name,
+        "local_seq_lens": {"requests": B, "us": round(ms_local * 1e3, 2),
+                           "requests_per_s": round(B / (ms_local * 1e-3), 1)},
+        "slot_mapping_decode": {"tokens": B, "us": round(ms_dec * 1e3, 2),
+                                "tokens_per_s": round(B / (ms_dec * 1e-3), 1)},
+        "slot_mapping_bulk": {"tokens": T, "ms": round(ms_bulk, 4), "tokens_per_s": round(T / (ms_bulk * 1e-3), 1),
+                              "gbs": round(bulk_bytes / (ms_bulk * 1e-3) / 1e9, 2)},
+        "cpu_baseline": None,
+    }
+    if cpu_budget_s > 0:
+        from oracle import layout as olay
+        pos_np, req_np = bulk_pos.cpu().numpy(), bulk_req.cpu().numpy()
+        spent, done, chunk = 0.0, 0, 1 << 16
+        while spent < cpu_budget_s and done < T:
+            hi = min(T, done + chunk)
+            t0 = time.perf_counter()
+            olay.slot_mapping(pos_np[done:hi], req_np[done:hi], table, w.block_size, D, w.interleave)
+            spent += time.perf_counter() - t0
+            done = hi
+        cores, blas = host_cores()
+        res["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"brute-force mapper over the first {done} of the bulk fill's {T} tokens; "
+                                         f"{spent:.1f} s", "host_cores": cores}
+        res["slot_mapping_bulk"]["speedup_gpu_over_oracle"] = round(res["slot_mapping_bulk"]["tokens_per_s"] /
+                                                                   res["cpu_baseline"]["value"], 1)
+    del bulk_pos, bulk_req, bulk_slots
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help=f"one workload only (default: {DEFAULT_WORKLOAD} as the headline, plus the per-config block)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--per-config-cpu-budget-s", type=float, default=4.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--calibrate-hbm", type=int, default=0, metavar="BYTES",
                     help="only run reference kernels for the HBM counters: a plain read (sum) of BYTES bytes "
                          "and a plain device copy of BYTES bytes, 5 times each")
@@ -646,11 +862,8 @@ def main():
               "runs on more than one GPU are not part of this build.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    import sequence_sharded_paged_amd as dcp
-    from tests.harness import DeviceInputs
-    from workloads import get_workload, make_case
+    from workloads import get_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -668,68 +881,40 @@ def main():
         print(json.dumps({"calibrate_hbm_bytes": args.calibrate_hbm, "reads": 5, "copies": 5,
                           "check": float(acc) / 5 / src.numel()}))
         return
-    if args.workload.startswith("kvw_"):
-        bench_kv_write(args, args.workload)
+    name = args.workload or DEFAULT_WORKLOAD
+    if name.startswith("kvw_"):
+        bench_kv_write(args, name)
         return
-    if args.workload.startswith("gather_"):
-        bench_gather(args, args.workload)
+    if name.startswith("gather_"):
+        bench_gather(args, name)
         return
     from workloads import SEGMENT_WORKLOADS, VERIFY_WORKLOADS
-    if args.workload in VERIFY_WORKLOADS:
-        bench_verify(args, VERIFY_WORKLOADS[args.workload])
+    if name in VERIFY_WORKLOADS:
+        bench_verify(args, VERIFY_WORKLOADS[name])
         return
-    if args.workload in SEGMENT_WORKLOADS:
-        bench_segment(args, SEGMENT_WORKLOADS[args.workload])
+    if name in SEGMENT_WORKLOADS:
+        bench_segment(args, SEGMENT_WORKLOADS[name])
         return
-    w = get_workload(args.workload)
-    t_gen = time.perf_counter()
-    case = make_case(w, device="cuda")
-    inp = DeviceInputs(case, "cuda", fill="zero")
-    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
-    torch.cuda.synchronize()
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] {w.name}: batch {case.batch}, {int(case.seq_lens.sum())} tokens, "
-          f"{case.kv_bytes() / 1e9:.3f} GB KV, inputs ready in {t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    for _ in range(args.warmup):
-        inp.step()
-    torch.cuda.synchronize()
-
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dcp.native.dcp_profile_enable(True)
-    dcp.native.dcp_profile_collect()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        inp.step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern_ms, launches = dcp.native.dcp_profile_collect()
-    dcp.native.dcp_profile_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    kern_avg_ms = kern_ms / max(launches, 1)
-
-    kv_bytes = case.kv_bytes()
-    value = kv_bytes / (ms * 1e-3) / 1e9
-    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
-    family = kernel_family(w)
-    traffic = load_traffic(family, w.name)
+    w = get_workload(name)
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget_s
+    head = measure_decode(w, args.steps, args.warmup, cpu)
+    cores, blas = host_cores()
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["kv_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": head["dtype"],
         "data": "synthetic",
         "config": {
             "workload": w.name,
-            "batch": case.batch,
+            "batch": head["batch"],
             "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads,
             "head_dim_k": w.head_dim_k,
@@ -738,25 +923,42 @@ def main():
             "block_size": w.block_size,
             "dcp_size": w.dcp_size,
             "interleave": w.interleave,
-            "tokens": int(case.seq_lens.astype(np.int64).sum()),
-            "kv_bytes": int(kv_bytes),
-            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-            "merged_queries_per_s": round(case.batch / (ms * 1e-3), 1),
-            "kernel": KERNEL_NAMES[family],
+            "tokens": head["tokens"],
+            "kv_bytes": head["algorithmic_bytes"]["kv"],
+            "pct_hbm_peak": head["pct_hbm_peak"],
+            "merged_queries_per_s": head["merged_queries_per_s"],
+            "algorithmic_bytes": head["algorithmic_bytes"],
+            "algorithmic_total_gbs": head["algorithmic_total_gbs"],
+            "step_overhead_ms": head["step_overhead_ms"],
+            "kernel": head["kernel"],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_avg_ms": round(kern_avg_ms, 5),
-        },
+        "roofline": head["roofline"],
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+    if head["cpu_baseline"] is not None:
+        cb = dict(head["cpu_baseline"])
+        cb["cores"] = blas
+        cb["host_cores"] = cores
+        cb["blas_threads"] = blas
+        out["cpu_baseline"] = cb
+    if args.workload is None and not args.no_per_config:
+        pc_cpu = 0.0 if args.no_cpu_baseline else args.per_config_cpu_budget_s
+        per = {}
+        for pname in PER_CONFIG:
+            if pname == w.name:
+                per[pname] = {k: v for k, v in head.items() if k != "cpu_baseline"}
+                per[pname]["cpu_baseline"] = out["cpu_baseline"]
+                continue
+            pw = get_workload(pname)
+            r = measure_decode(pw, max(5, args.steps // 2), args.warmup, pc_cpu)
+            if r["cpu_baseline"] is not None:
+                r["cpu_baseline"]["host_cores"] = cores
+                r["cpu_baseline"]["blas_threads"] = blas
+            per[pname] = r
+            print(f"[bench] {pname}: step {r['ms_per_step']:.3f} ms, {r['kv_gbs']:.0f} GB/s "
+                  f"({r['pct_hbm_peak']:.1f}%), kernel frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+        out["per_config"] = per
+        out["layout"] = measure_layout(w, 50, pc_cpu)
     print(json.dumps(out), flush=True)
 
 

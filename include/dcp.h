@@ -174,9 +174,9 @@ typedef struct dcp_kv_cache {
   int32_t num_kv_heads;
   int32_t head_dim_k;
   int32_t head_dim_v;
-  const void* k;
+  void* k;                    /* device; written only by dcp_kv_cache_write */
   int64_t k_stride[5];        /* rank, block, head, token, dim (elements) */
-  const void* v;              /* NULL: V aliases K[..., 0:head_dim_v] */
+  void* v;                    /* NULL: V aliases K[..., 0:head_dim_v] */
   int64_t v_stride[5];
   const float* k_scale;       /* [num_kv_heads], fp8 only, else NULL */
   const float* v_scale;       /* [num_kv_heads], fp8 only, else NULL */
@@ -185,8 +185,11 @@ typedef struct dcp_kv_cache {
 /*
  * dcp_partial_decode_attn_workspace_size - bytes of device workspace that
  * dcp_partial_decode_attn needs for these arguments (0 is possible). Host
- * only; depends on no device state. Returns 0 and sets *status (if non-NULL)
- * to an error code when the arguments are invalid.
+ * only: it reads no device memory, but the MFMA kernels size their split
+ * pieces by the number of persistent workers the current device runs (its
+ * compute-unit count), so the size holds for calls on the current device (and
+ * devices of the same model). Returns 0 and sets *status (if non-NULL) to an
+ * error code when the arguments are invalid.
  */
 size_t dcp_partial_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
                                               int32_t q_dtype, const dcp_kv_cache_t* kv,
@@ -400,8 +403,8 @@ int dcp_lse_merge(const float* part_o, const float* part_lse, int32_t num_parts,
  * num_tokens >= 0 (0: nothing is launched)
  * slots      device, [num_ranks, num_tokens] int64 (as from dcp_slot_mapping)
  * num_ranks  1..64: pools kv describes, counted from the pool kv->k points to
- * kv         the pools to write (k and v are written through despite the
- *            const in dcp_kv_cache_t); head_dim_k and head_dim_v multiples
+ * kv         the pools to write (the descriptor is not modified; the pools
+ *            its k and v point to are); head_dim_k and head_dim_v multiples
  *            of 8; fp8 needs k_scale (and v_scale when v != NULL)
  * Errors: DCP_ERR_INVALID_ARG (sizes, NULL pointers, v_new / kv->v mismatch,
  * fp8 without scales), DCP_ERR_UNSUPPORTED (src_dtype, head dims not

@@ -13,8 +13,8 @@ pool). Layouts:
 * MLA: no V tensor; the value is the first ``head_dim_v`` entries of the K
   row (one latent vector serves as key and value).
 
-``write`` places canonical rows at the slots ``dcp_slot_mapping`` produced
-(a torch scatter; cache population is set-up, not part of the decode step).
+The pools are filled by ``dcp_kv_cache_write`` (new rows quantised to the
+pool format at the slots ``dcp_slot_mapping`` produced).
 """
 
 import torch
@@ -76,26 +76,6 @@ class PagedKVCache:
         d.k_scale = None if self.k_scale is None else self.k_scale.data_ptr()
         d.v_scale = None if self.v_scale is None else self.v_scale.data_ptr()
         return d
-
-    def write(self, slots, k_rows, v_rows=None):
-        """Scatter canonical rows ``k_rows [T, Hkv, Dk]`` (and ``v_rows``) to
-        ``slots [num_ranks, T]`` (-1 = not on that rank)."""
-        bs = self.block_size
-        kraw, kin = _raw(self.k), _raw(k_rows)
-        vraw = None if self.v is None else _raw(self.v)
-        vin = None if v_rows is None else _raw(v_rows)
-        for r in range(self.num_ranks):
-            sel = slots[r] >= 0
-            s = slots[r][sel]
-            if s.numel() == 0:
-                continue
-            blk, off = s // bs, s % bs
-            kraw[r][blk, :, off, :] = kin[sel]
-            if vraw is not None:
-                if self.v_layout == "dim_major":
-                    vraw[r][blk, :, :, off] = vin[sel]
-                else:
-                    vraw[r][blk, :, off, :] = vin[sel]
 
 
 def _raw(t):

@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
   const int n = lane & 15, qd = lane >> 4;
   const int G = p.group, rows = p.tpu * G;
   const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, kGqaMaxWorkers);
+  SplitWs ws = split_ws(p.workspace, U, workers);
   const int64_t T = ws.prefix[U];
   if (worker >= workers || T == 0) return;
   const int64_t tpw = (T + workers - 1) / workers;
@@ -409,10 +409,6 @@ bool gqa_supported(const AttnParams& p) {
   return true;
 }
 
-size_t gqa_workspace_bytes(const AttnParams& p) {
-  return split_ws_bytes(split_units_host(p), kGqaMaxWorkers, p.tpu * p.group, kGqaDim);
-}
-
 // Persistent wavefronts the device holds at once, cached per device (static
 // storage starts zeroed; concurrent first calls store the same value).
 template <bool kFp8>
@@ -430,11 +426,17 @@ static int gqa_workers() {
   return c;
 }
 
+// Sized for the workers this device runs (split pieces: two per worker).
+size_t gqa_workspace_bytes(const AttnParams& p) {
+  const int workers = p.kv.dtype == DCP_FP8_E4M3 ? gqa_workers<true>() : gqa_workers<false>();
+  return split_ws_bytes(split_units_host(p), workers, p.tpu * p.group, kGqaDim);
+}
+
 hipError_t launch_gqa_attn(const AttnParams& p) {
   const bool fp8 = p.kv.dtype == DCP_FP8_E4M3;
   const int workers = fp8 ? gqa_workers<true>() : gqa_workers<false>();
   const int tok = fp8 ? GqaTile<true>::TOK : GqaTile<false>::TOK;
-  launch_split_plan(p, tok, workers, kGqaMaxWorkers);
+  launch_split_plan(p, tok, workers);
   const dim3 grid((workers + kGqaWavesPerBlock - 1) / kGqaWavesPerBlock);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   if (fp8)
@@ -442,7 +444,7 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   else
     hipLaunchKernelGGL(gqa_attn_kernel<false>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  launch_split_combine<kGqaDim>(p, workers, kGqaMaxWorkers);
+  launch_split_combine<kGqaDim>(p, workers);
   return hipGetLastError();
 }
 

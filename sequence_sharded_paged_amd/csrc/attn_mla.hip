@@ -183,7 +183,7 @@ mla_attn_kernel(AttnParams p, int workers) {
   const int n = lane & 15, g = lane >> 4;
   const int worker = blockIdx.x;
   const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, kMlaMaxWorkers);
+  SplitWs ws = split_ws(p.workspace, U, workers);
   const int64_t T = ld_uniform(ws.prefix + U);
   if (T == 0 || worker >= workers) return;
   const int64_t tpw = (T + workers - 1) / workers;
@@ -742,17 +742,20 @@ bool mla_supported(const AttnParams& p) {
   return true;
 }
 
+// One persistent workgroup per CU; the workspace is sized for that many.
+static int mla_workers() { return min(kMlaMaxWorkers, device_cu_count()); }
+
 size_t mla_workspace_bytes(const AttnParams& p) {
-  return split_ws_bytes(split_units_host(p), kMlaMaxWorkers, kMlaHeads, kMlaDv);
+  return split_ws_bytes(split_units_host(p), mla_workers(), kMlaHeads, kMlaDv);
 }
 
 hipError_t launch_mla_attn(const AttnParams& p) {
-  const int workers = min(kMlaMaxWorkers, device_cu_count());
-  launch_split_plan(p, kMlaTile, workers, kMlaMaxWorkers);
+  const int workers = mla_workers();
+  launch_split_plan(p, kMlaTile, workers);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   hipLaunchKernelGGL(mla_attn_kernel, dim3(workers), dim3(kMlaThreads), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  launch_split_combine<kMlaDv>(p, workers, kMlaMaxWorkers);
+  launch_split_combine<kMlaDv>(p, workers);
   return hipGetLastError();
 }
 

@@ -294,16 +294,22 @@ constexpr int kXcds = 8;        // XCDs of an MI355X; workgroup i runs on XCD i 
 constexpr int kVtDims = 128;    // V dims per tile
 constexpr int kVtPitch = 136;   // LDS row pitch in elements (8-element chunks stay 16-byte aligned)
 
-// Wave 0 of kv_vt_kernel, one owner pass: f[lane] = (owner << kSlotBits) |
-// slot of tile token `lane` at this pass's owner (all ones: none). Groups the
-// tokens by the aligned 4-element word of the pool that their V row offset
-// (head 0, dim 0) falls in: the rows are ranked (a sort by offset, done with
-// per-lane counting) and permuted into sorted order, so tokens sharing a
-// word are adjacent; group g's word starts at element s_gbase[g] and
-// s_gtok[4 g + u] is the token stored at its element u (-1: none). Returns
-// the number of tokens with an owner.
-__device__ __forceinline__ int vt_group_pass(const KvWriteParams& p, int lane, int ntok, uint64_t f,
-                                             int* s_gtok, int64_t* s_gbase, int* s_groups) {
+// Wave 0 of the V^T kernels, one owner pass: f[lane] = (owner << kSlotBits) |
+// slot of tile token `lane` at this pass's owner (all ones: none). The tokens
+// with an owner are ranked by the pool offset of their V row (head 0, dim 0)
+// with per-lane counting (ties by token) and permuted into that order, then
+// grouped by the aligned word of 2^log_w elements their offset falls in.
+// Lane i < nvalid receives the i-th token in order: its index (tok), its
+// offset (vs) and group (g, counted in order); bit i of `starts` is set when
+// it opens its group.
+struct VtOrder {
+  int tok, g, nvalid;
+  int64_t vs;
+  bool in;
+  uint64_t starts;
+};
+
+__device__ __forceinline__ VtOrder vt_order(const KvWriteParams& p, int lane, int ntok, uint64_t f, int log_w) {
   const bool valid = lane < ntok && f != ~uint64_t(0);
   int64_t vr = 0;
   if (valid) {
@@ -315,8 +321,7 @@ __device__ __forceinline__ int vt_group_pass(const KvWriteParams& p, int lane, i
   const uint64_t vmask = __builtin_amdgcn_ballot_w64(valid);
   const int nvalid = __builtin_popcountll(vmask);
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  // position in the order (valid first, by offset, ties by token)
-  int rank;
+  int rank;  // position in the order (valid first, by offset, ties by token)
   if (valid) {
     rank = 0;
     for (uint64_t m = vmask; m; m &= m - 1) {
@@ -328,15 +333,30 @@ __device__ __forceinline__ int vt_group_pass(const KvWriteParams& p, int lane, i
     rank = nvalid + __builtin_popcountll(~vmask & below);
   }
   // lane `rank` receives (token, offset)
-  const int tok = __builtin_amdgcn_ds_permute(rank * 4, lane);
+  VtOrder o;
+  o.tok = __builtin_amdgcn_ds_permute(rank * 4, lane);
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr >> 32)));
-  const int64_t vs = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-  const int64_t word = vs >> 2;
+  o.vs = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  const int64_t word = o.vs >> log_w;
   const int64_t prev = __shfl(word, lane == 0 ? 0 : lane - 1, 64);
-  const bool in = lane < nvalid;
-  const uint64_t starts = __builtin_amdgcn_ballot_w64(in && (lane == 0 || word != prev));
-  const int g = __builtin_popcountll(starts & ((below << 1) | 1)) - 1;
+  o.nvalid = nvalid;
+  o.in = lane < nvalid;
+  o.starts = __builtin_amdgcn_ballot_w64(o.in && (lane == 0 || word != prev));
+  o.g = __builtin_popcountll(o.starts & ((below << 1) | 1)) - 1;
+  return o;
+}
+
+// kv_vt_kernel's grouping by aligned 4-element words: group g's word starts
+// at element s_gbase[g] and s_gtok[4 g + u] is the token stored at its
+// element u (-1: none). Returns the number of tokens with an owner.
+__device__ __forceinline__ int vt_group_pass(const KvWriteParams& p, int lane, int ntok, uint64_t f,
+                                             int* s_gtok, int64_t* s_gbase, int* s_groups) {
+  const VtOrder o = vt_order(p, lane, ntok, f, 2);
+  const int tok = o.tok, g = o.g;
+  const int64_t vs = o.vs, word = vs >> 2;
+  const bool in = o.in;
+  const uint64_t starts = o.starts;
 #pragma unroll
   for (int u = 0; u < 4; ++u) s_gtok[4 * lane + u] = -1;
   if (in) {
@@ -344,7 +364,7 @@ __device__ __forceinline__ int vt_group_pass(const KvWriteParams& p, int lane, i
     if ((starts >> lane) & 1) s_gbase[g] = word * 4;
   }
   if (lane == 0) *s_groups = __builtin_popcountll(starts);
-  return nvalid;
+  return o.nvalid;
 }
 
 // Large batches, V stored token-contiguous inside a block ([block, head,
@@ -382,7 +402,7 @@ __global__ void __launch_bounds__(256) kv_vt_kernel(KvWriteParams p) {
   const int nd = dv - ds < kVtDims ? dv - ds : kVtDims;
   const int cpt = nd / 8, total = ntok * cpt;  // <= 1024
   const int64_t cap = static_cast<int64_t>(p.kv.num_blocks) * p.kv.block_size;
-  St* vpool = static_cast<St*>(const_cast<void*>(p.kv.v));
+  St* vpool = static_cast<St*>(p.kv.v);
   const int64_t vdim = p.kv.v_stride[4], vhead = p.kv.v_stride[2];
 
   auto load_head = [&](int h, Raw8<kSrcBf16> (&raw)[4]) __attribute__((always_inline)) {
@@ -517,37 +537,11 @@ template <int kW>
 __device__ __forceinline__ int vt16_group_pass(const KvWriteParams& p, int lane, int ntok, uint64_t f,
                                                uint32_t* s_gmask, int64_t* s_gbase, int* s_col, int* s_groups) {
   constexpr int kLog = kW == 16 ? 4 : kW == 8 ? 3 : 2;
-  const bool valid = lane < ntok && f != ~uint64_t(0);
-  int64_t vr = 0;
-  if (valid) {
-    const int rk = static_cast<int>(f >> kSlotBits);
-    const int64_t s = static_cast<int64_t>(f & ((uint64_t(1) << kSlotBits) - 1));
-    const int64_t blk = s / p.kv.block_size, off = s - blk * p.kv.block_size;
-    vr = rk * p.kv.v_stride[0] + blk * p.kv.v_stride[1] + off * p.kv.v_stride[3];
-  }
-  const uint64_t vmask = __builtin_amdgcn_ballot_w64(valid);
-  const int nvalid = __builtin_popcountll(vmask);
-  const uint64_t below = (uint64_t(1) << lane) - 1;
-  int rank;  // position in the order (valid first, by offset, ties by token)
-  if (valid) {
-    rank = 0;
-    for (uint64_t m = vmask; m; m &= m - 1) {
-      const int jl = __builtin_ctzll(m);
-      const int64_t vj = __shfl(vr, jl, 64);
-      rank += (vj < vr) || (vj == vr && jl < lane);
-    }
-  } else {
-    rank = nvalid + __builtin_popcountll(~vmask & below);
-  }
-  const int tok = __builtin_amdgcn_ds_permute(rank * 4, lane);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_permute(rank * 4, static_cast<int>(vr >> 32)));
-  const int64_t vs = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-  const int64_t word = vs >> kLog;
-  const int64_t prev = __shfl(word, lane == 0 ? 0 : lane - 1, 64);
-  const bool in = lane < nvalid;
-  const uint64_t starts = __builtin_amdgcn_ballot_w64(in && (lane == 0 || word != prev));
-  const int g = __builtin_popcountll(starts & ((below << 1) | 1)) - 1;
+  const VtOrder o = vt_order(p, lane, ntok, f, kLog);
+  const int tok = o.tok, g = o.g;
+  const int64_t vs = o.vs, word = vs >> kLog;
+  const bool in = o.in;
+  const uint64_t starts = o.starts;
   s_gmask[lane] = 0;
   s_col[lane] = -1;
   __builtin_amdgcn_wave_barrier();
@@ -558,7 +552,7 @@ __device__ __forceinline__ int vt16_group_pass(const KvWriteParams& p, int lane,
     if ((starts >> lane) & 1) s_gbase[g] = word * kW;
   }
   if (lane == 0) *s_groups = __builtin_popcountll(starts);
-  return nvalid;
+  return o.nvalid;
 }
 
 template <int kDst, bool kSrcBf16>
@@ -586,7 +580,7 @@ __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
   const int nd = dv - ds < kVtDims ? dv - ds : kVtDims;
   const int cpt = nd / 8, total = ntok * cpt;  // <= 1024
   const int64_t cap = static_cast<int64_t>(p.kv.num_blocks) * p.kv.block_size;
-  St* vpool = static_cast<St*>(const_cast<void*>(p.kv.v));
+  St* vpool = static_cast<St*>(p.kv.v);
   const int64_t vdim = p.kv.v_stride[4], vhead = p.kv.v_stride[2];
   char* cells = reinterpret_cast<char*>(s_cell);
   // this thread's chunks (token, first dim), fixed for the whole tile (-1: none)
@@ -796,7 +790,7 @@ __global__ void __launch_bounds__(256) kv_scatter_kernel(KvWriteParams p) {
         const int64_t* st = is_v ? p.kv.v_stride : p.kv.k_stride;
         const int64_t d0 = is_v ? c - ck : c;
         const int64_t e = r * st[0] + blk * st[1] + h * st[2] + off * st[3] + d0 * 8 * st[4];
-        store8<kDst>(const_cast<void*>(is_v ? p.kv.v : p.kv.k), e, st[4], is_v ? p.vec_v : p.vec_k, q[j]);
+        store8<kDst>(is_v ? p.kv.v : p.kv.k, e, st[4], is_v ? p.vec_v : p.vec_k, q[j]);
       }
     }
   }
@@ -900,10 +894,10 @@ static void launch_typed(const KvWriteParams& p, hipStream_t stream) {
                        0, stream, p);
     return;
   }
-  auto rows = [&](const void* src, const void* pool, const int64_t* st, const float* scale, int dim, int vec) {
+  auto rows = [&](const void* src, void* pool, const int64_t* st, const float* scale, int dim, int vec) {
     RowsArgs a;
     a.src = src;
-    a.pool = const_cast<void*>(pool);
+    a.pool = pool;
     for (int i = 0; i < 5; ++i) a.st[i] = st[i];
     a.scale = scale;
     a.dim = dim;

@@ -29,11 +29,13 @@ constexpr int kPartExtra = 4;
 
 struct SplitWs {
   int64_t* prefix;  // [U + 1] tile prefix over units; prefix[U] = total tiles
-  int32_t* wunit;   // [max_workers] unit holding each worker's first tile
-  int32_t* todo;    // [1 + U + max_workers]: count, then the units that are empty or cut
-  float* part;      // [max_workers][2][rows][Dv + kPartExtra], rows = tpu * group
+  int32_t* wunit;   // [workers] unit holding each worker's first tile
+  int32_t* todo;    // [1 + U + workers]: count, then the units that are empty or cut
+  float* part;      // [workers][2][rows][Dv + kPartExtra], rows = tpu * group
 };
 
+// The layout depends on the number of workers the launch uses (fixed per
+// device), so the size query and every kernel of a call agree on it.
 __host__ __device__ inline SplitWs split_ws(void* base, int64_t units, int max_workers) {
   SplitWs w;
   char* p = static_cast<char*>(base);
@@ -117,13 +119,12 @@ __device__ __forceinline__ int64_t ceil_div_fp64(int64_t a, int64_t b) {
 // thread takes a contiguous range of pairs, so a unit's position is a loop
 // counter rather than a decomposition of its index (64-bit divisions are
 // software routines, and on one CU they set the planner's time).
-static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnParams p, int tok_log2, int workers,
-                                                                         int max_workers) {
+static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnParams p, int tok_log2, int workers) {
   __shared__ int64_t wsum[kPlanThreads / 64];
   __shared__ int64_t total_s;
   __shared__ int todo_n;
   const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, max_workers);
+  SplitWs ws = split_ws(p.workspace, U, workers);
   const int H = p.kv.num_kv_heads, ntg = p.ntg;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int RB = p.rank_count * p.batch;  // (rank, request) pairs; U < 2^31
@@ -192,8 +193,7 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
 // before the first is used; a unit cut into at most four pieces (the usual
 // case) takes its maximum from the same loads.
 template <int kDv>
-__global__ void __launch_bounds__(kCombineThreads) split_combine_kernel(AttnParams p, int workers, int max_workers,
-                                                                       int vec_out) {
+__global__ void __launch_bounds__(kCombineThreads) split_combine_kernel(AttnParams p, int workers, int vec_out) {
   constexpr int kVec = kDv >= 256 ? 4 : kDv / 64;  // floats per lane per load
   constexpr int kRounds = kDv / (64 * kVec);
   static_assert(kVec == 2 || kVec == 4, "combine widths");
@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(kCombineThreads) split_combine_kernel(AttnPara
   constexpr int kBatch = 4;
   const int G = p.group, rows = p.tpu * p.group;
   const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, max_workers);
+  SplitWs ws = split_ws(p.workspace, U, workers);
   const int64_t T = ws.prefix[U];
   const int64_t tpw = T > 0 ? (T + workers - 1) / workers : 1;
   const int64_t items = static_cast<int64_t>(ws.todo[0]) * rows;
@@ -308,17 +308,16 @@ static inline int log2_exact(int x) {
   return l;
 }
 
-static inline void launch_split_plan(const AttnParams& p, int tok, int workers, int max_workers) {
-  hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, log2_exact(tok), workers,
-                     max_workers);
+static inline void launch_split_plan(const AttnParams& p, int tok, int workers) {
+  hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kPlanThreads), 0, p.stream, p, log2_exact(tok), workers);
 }
 
 // Eight workgroups of four wavefronts per CU: every SIMD holds eight items in flight.
 template <int kDv>
-static inline void launch_split_combine(const AttnParams& p, int workers, int max_workers) {
+static inline void launch_split_combine(const AttnParams& p, int workers) {
   const int vec_out = reinterpret_cast<uintptr_t>(p.out_o) % 16 == 0;
   hipLaunchKernelGGL(split_combine_kernel<kDv>, dim3(8 * device_cu_count()), dim3(kCombineThreads), 0, p.stream, p,
-                     workers, max_workers, vec_out);
+                     workers, vec_out);
 }
 
 }  // namespace dcp

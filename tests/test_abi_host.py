@@ -262,7 +262,7 @@ def test_product_path_loads_no_oracle():
     the tests' checks and bench.py's cpu_baseline functions)."""
     import subprocess
     import sys
-    code = ("import sys; import sequence_sharded_paged_amd, workloads, workloads.generate, tests.harness; "
+    code = ("import sys; import sequence_sharded_paged_amd, workloads, workloads.generate, workloads.device; "
             "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
             "assert not bad, bad")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

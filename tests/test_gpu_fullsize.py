@@ -1,19 +1,46 @@
 """GPU parity at the workloads' full sizes, in the launch configuration that
-bench.py times (all ranks, MFMA kernels, the same seeded batch). The oracle
-recomputes a sample of requests one by one (shortest, median, longest, and
-one seeded pick): merged output against full softmax over the unsharded
-sequence, and every rank's partial against the oracle's partial over the
-tokens that rank owns."""
+bench.py times (all ranks, MFMA kernels, the same seeded batch, pools
+pre-filled with NaN bit patterns so that a read of an unwritten slot
+poisons the result). Every request's merged output and LSE is compared with
+the float64 oracle (full softmax over the unsharded sequence); every rank's
+partial is compared with the oracle's partial over the tokens that rank owns
+for a sample of requests (shortest, median, longest, one seeded pick).
+
+Each workload runs once on the GPU; its requests are then checked in chunks
+(one test per chunk), so that no single test holds the CPU oracle for long.
+"""
+
+import gc
 
 import numpy as np
 import pytest
 import torch
 
 import sequence_sharded_paged_amd as dcp
-from tests.harness import DeviceInputs, check_against_oracle
+from tests.harness import check_against_oracle, check_segment_against_oracle, check_verify_against_oracle
 from workloads import get_workload, make_case
+from workloads.device import DeviceInputs
 
 pytestmark = pytest.mark.gpu
+
+_RUN = {}  # the one workload whose GPU result is held: name -> (inputs, extra, host result)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _release_at_end():
+    yield
+    _RUN.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _hold(name, make):
+    if name not in _RUN:
+        _RUN.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        _RUN[name] = make()
+    return _RUN[name]
 
 
 def _sample(lens, seed):
@@ -23,61 +50,100 @@ def _sample(lens, seed):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,max_requests", [("gqa_fp8_binned", 4), ("mla_bf16_bimodal", 4),
-                                               ("mla_bf16_longtail_sink", 2)])
-def test_full_size_sampled(device, name, max_requests):
-    w = get_workload(name)
-    case = make_case(w, device=device)
-    inp = DeviceInputs(case, device, fill="zero")
-    res = inp.run(algo=dcp.DCP_ALGO_AUTO)
-    # properties at full size for every request: finite outputs, LSE defined
-    o, lse = res[2].float(), res[3]
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    reqs = _sample(case.seq_lens, w.seed)[:max_requests] if max_requests < 4 else _sample(case.seq_lens, w.seed)
-    if name == "mla_bf16_longtail_sink":
-        order = np.argsort(case.seq_lens)
-        reqs = [int(order[0]), int(order[-1])]
-    print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
-    check_against_oracle(inp, res, requests=reqs)
+def _chunk(n, i, k):
+    lo, hi = (n * i) // k, (n * (i + 1)) // k
+    return list(range(lo, hi))
 
 
-@pytest.mark.parametrize("name", ["gqa_fp8_binned_q2", "gqa_bf16_32k_q4", "mla_bf16_bimodal_q2"])
-def test_verify_full_size_sampled(device, name):
+DECODE = [("gqa_fp8_binned", 8), ("mla_bf16_bimodal", 4), ("mla_bf16_longtail_sink", 4)]
+
+
+@pytest.mark.parametrize("name,chunk,chunks", [(n, i, k) for n, k in DECODE for i in range(k)])
+def test_full_size_every_request(device, name, chunk, chunks):
+    def make():
+        w = get_workload(name)
+        case = make_case(w, device=device)
+        inp = DeviceInputs(case, device, fill="nan")
+        res = inp.run(algo=dcp.DCP_ALGO_AUTO)
+        o, lse = res[2].float(), res[3]
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        host = tuple(t.float().cpu() for t in res)
+        return inp, None, host
+    inp, _, host = _hold(name, make)
+    case = inp.case
+    reqs = _chunk(case.batch, chunk, chunks)
+    sampled = [b for b in _sample(case.seq_lens, case.workload.seed) if b in reqs]
+    print(f"{name}: requests {reqs[0]}..{reqs[-1]} ({int(case.seq_lens[reqs].sum())} tokens), "
+          f"partials of {sampled}", flush=True)
+    check_against_oracle(inp, host, requests=[b for b in reqs if b not in sampled], check_parts=False)
+    if sampled:
+        check_against_oracle(inp, host, requests=sampled)
+
+
+VERIFY = [("gqa_fp8_binned_q2", 8), ("gqa_bf16_32k_q4", 1), ("mla_bf16_bimodal_q2", 4)]
+
+
+@pytest.mark.parametrize("name,chunk,chunks", [(n, i, k) for n, k in VERIFY for i in range(k)])
+def test_verify_full_size_every_request(device, name, chunk, chunks):
     """Multi-token decode at the verification workloads' full sizes, in the
-    launch configuration bench.py times; sampled requests against the oracle."""
-    from tests.harness import VerifyRun, check_verify_against_oracle
+    launch configuration bench.py times."""
     from workloads import get_verify_workload, make_verify_queries
-    vw = get_verify_workload(name)
-    w = vw.geometry()
-    case = make_case(w, device=device)
-    inp = DeviceInputs(case, device, fill="zero")
-    run = VerifyRun(inp, make_verify_queries(w, case.batch, vw.q_len, device), algo=dcp.DCP_ALGO_AUTO)
-    res = run.run()
-    assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
-    reqs = _sample(case.seq_lens, w.seed + 1)[:3]
-    print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
-    check_verify_against_oracle(run, res, requests=reqs)
+    from workloads.device import VerifyRun
+
+    def make():
+        vw = get_verify_workload(name)
+        w = vw.geometry()
+        case = make_case(w, device=device)
+        inp = DeviceInputs(case, device, fill="nan")
+        run = VerifyRun(inp, make_verify_queries(w, case.batch, vw.q_len, device), algo=dcp.DCP_ALGO_AUTO)
+        res = run.run()
+        assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
+        host = tuple(t.float().cpu() for t in res)
+        run.q = run.q.cpu()
+        return inp, run, host
+    inp, run, host = _hold(name, make)
+    case = inp.case
+    reqs = _chunk(case.batch, chunk, chunks)
+    sampled = [b for b in _sample(case.seq_lens, case.workload.seed + 1)[:3] if b in reqs]
+    print(f"{name}: requests {reqs[0]}..{reqs[-1]}, partials of {sampled}", flush=True)
+    check_verify_against_oracle(run, host, requests=[b for b in reqs if b not in sampled], check_parts=False)
+    if sampled:
+        check_verify_against_oracle(run, host, requests=sampled)
 
 
-@pytest.mark.parametrize("name", ["mla_bf16_longtail_sink_swa128", "gqa_fp8_binned_swa128"])
-def test_segment_full_size_sampled(device, name):
+SEGMENT = [("mla_bf16_longtail_sink_swa128", 2), ("gqa_fp8_binned_swa128", 8)]
+
+
+@pytest.mark.parametrize("name,chunk,chunks", [(n, i, k) for n, k in SEGMENT for i in range(k)])
+def test_segment_full_size_every_request(device, name, chunk, chunks):
     """Decode with a replicated segment at full size, in bench.py's launch
-    configuration; sampled requests against the oracle."""
-    from tests.harness import SegmentInputs, check_segment_against_oracle
+    configuration."""
     from workloads import get_segment_workload, make_segment
+    from workloads.device import SegmentInputs
+
     sw = get_segment_workload(name)
-    w = sw.geometry()
-    case = make_case(w, device=device)
-    inp = DeviceInputs(case, device, fill="zero")
-    seg = make_segment(w, case.seq_lens, sw.window, case.k_scale, case.v_scale, device)
-    sgi = SegmentInputs(inp, seg, device)
-    inp.prepare(algo=dcp.DCP_ALGO_AUTO)
-    inp.partial()
-    sgi.fold(sw.seg_rank)
-    inp.merge()
-    torch.cuda.synchronize()
-    res = (inp.po, inp.pl, inp.o, inp.lse)
-    assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
-    reqs = _sample(case.seq_lens, w.seed + 2)[:2]
-    print(f"{name}: checking requests {reqs} of lengths {[int(case.seq_lens[b]) for b in reqs]}", flush=True)
-    check_segment_against_oracle(inp, seg, sw.seg_rank, res, requests=reqs)
+
+    def make():
+        w = sw.geometry()
+        case = make_case(w, device=device)
+        inp = DeviceInputs(case, device, fill="nan")
+        seg = make_segment(w, case.seq_lens, sw.window, case.k_scale, case.v_scale, device)
+        sgi = SegmentInputs(inp, seg, device)
+        inp.prepare(algo=dcp.DCP_ALGO_AUTO)
+        inp.partial()
+        sgi.fold(sw.seg_rank)
+        inp.merge()
+        torch.cuda.synchronize()
+        res = (inp.po, inp.pl, inp.o, inp.lse)
+        assert torch.isfinite(res[2].float()).all() and torch.isfinite(res[3]).all()
+        host = tuple(t.float().cpu() for t in res)
+        return inp, seg, host
+    inp, seg, host = _hold(name, make)
+    case = inp.case
+    reqs = _chunk(case.batch, chunk, chunks)
+    sampled = [b for b in _sample(case.seq_lens, case.workload.seed + 2)[:2] if b in reqs]
+    print(f"{name}: requests {reqs[0]}..{reqs[-1]}, partials of {sampled}", flush=True)
+    check_segment_against_oracle(inp, seg, sw.seg_rank, host, requests=[b for b in reqs if b not in sampled],
+                                 check_parts=False)
+    if sampled:
+        check_segment_against_oracle(inp, seg, sw.seg_rank, host, requests=sampled)
