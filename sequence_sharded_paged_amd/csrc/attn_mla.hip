@@ -195,7 +195,13 @@ mla_attn_kernel(AttnParams p, int workers) {
   const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks3 = p.kv.k_stride[3];
   const int row_bytes = static_cast<int>(ks3 * 2);  // bytes between consecutive tokens of a block
   const char* kbase = static_cast<const char*>(p.kv.k);
-  const float c2 = p.softmax_scale * DCP_LOG2E;
+  // The kernel masks a shard's tail tokens with -inf scores before scaling,
+  // which needs a positive scale: a negative one is carried by Q's sign bits
+  // (s c2 = (-s) (-c2), exact in bf16), a zero one by a zeroed Q and scale 1
+  // (every weight is then exp2(0 - m_ref), as with scale 0).
+  const float c2_in = p.softmax_scale * DCP_LOG2E;
+  const float c2 = c2_in > 0.f ? c2_in : (c2_in < 0.f ? -c2_in : 1.f);
+  const uint32_t q_keep = c2_in == 0.f ? 0u : 0xFFFFFFFFu, q_flip = c2_in < 0.f ? 0x80008000u : 0u;
   const uint32_t lds0 = lds_addr(lds);
   auto stage_of = [&](int64_t t) __attribute__((always_inline)) {
     return static_cast<int>((t - wstart) & (kMlaStages - 1));
@@ -455,6 +461,15 @@ mla_attn_kernel(AttnParams p, int workers) {
                             (lane & 31)) * kMlaDk + 8 * h;
 #pragma unroll
       for (int ks = 0; ks < kMlaKSteps; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * ks);
+      if (!(c2_in > 0.f)) {  // uniform
+#pragma unroll
+        for (int ks = 0; ks < kMlaKSteps; ++ks) {
+          u32x4_t w = __builtin_bit_cast(u32x4_t, qop[ks]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = (w[j] & q_keep) ^ q_flip;
+          qop[ks] = __builtin_bit_cast(bf16x8_t, w);
+        }
+      }
     }
     // Q is complete here, so no wait for it lands inside the tile loop (where
     // it would also drain the tiles in flight).

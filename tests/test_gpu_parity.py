@@ -136,6 +136,20 @@ def test_attention_small(device, name):
             check_against_oracle(inp, res)
 
 
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("scale", [0.0, -0.06])
+def test_nonpositive_softmax_scale(device, name, scale):
+    """A zero scale gives every cached token the same weight (the mean of V); a
+    negative one favours the lowest scores. Every shard has a ragged tail, so
+    the kernels' tail masks meet both."""
+    import dataclasses
+    w = dataclasses.replace(get_workload(name), scale_override=scale)
+    case = make_case(w, device=device, seq_lens=[1, 37, 600, 2049, 0] if name != "gqa_fp32_tiny" else None)
+    inp = DeviceInputs(case, device)
+    for algo in _algos(name):
+        check_against_oracle(inp, inp.run(algo=algo))
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_longtail_sink"])
 def test_rank_subsets(device, name):
     """One GPU computing only its own rank(s), as a per-GPU deployment would."""

@@ -62,6 +62,24 @@ def test_closed_forms():
         np.testing.assert_allclose(lse[h], 0.3 * q[h] @ k[0, h // 2] + np.log(L), rtol=1e-12)
 
 
+def test_nonpositive_scales():
+    """Scale 0: uniform weights whatever q is (mean of the values, LSE = ln L);
+    scale -c: the same result as scale c with q negated; both against torch."""
+    Hq, Hkv, D, L = 6, 3, 16, 50
+    q, k, v = _rand((Hq, D), 8), _rand((L, Hkv, D), 9), _rand((L, Hkv, D), 10)
+    o, lse = attention.decode_attention(q, k, v, 0.0)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[h], v[:, h // 2, :].mean(axis=0), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(L), rtol=1e-14)
+    o, lse = attention.decode_attention(q, k, v, -0.2)
+    o2, lse2 = attention.decode_attention(-q, k, v, 0.2)
+    np.testing.assert_allclose(o, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-13)
+    o_ref, lse_ref = _sdpa(q, k, v, -0.2)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
 def test_empty_and_sink_edge_cases():
     Hq, D = 4, 8
     q = _rand((Hq, D), 7)

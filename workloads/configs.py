@@ -34,9 +34,12 @@ class Workload:
     sink: bool = False        # per-query-head sink logit ~ N(0, 1)
     out_format: str = "fp32"  # merged output format
     description: str = ""
+    scale_override: float | None = None  # a test's softmax scale in place of 1 / sqrt(head_dim_k)
 
     @property
     def softmax_scale(self) -> float:
+        if self.scale_override is not None:
+            return self.scale_override
         return 1.0 / math.sqrt(self.head_dim_k)
 
     @property
