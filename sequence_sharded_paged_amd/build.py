@@ -30,29 +30,42 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is
+# built as usual): for the CPU-only checks of the C ABI's host paths.
+SANITIZE_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                  "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer").split()
+SANITIZED_LIB = os.path.join(ROOT, "_build", "sanitized", "libdcp.so")
+
+
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libdcp.so; with ``sanitize`` the host code is instrumented and the
+    library goes to ``_build/sanitized/`` (load it with the ASan runtime
+    preloaded)."""
+    objdir = os.path.join(ROOT, "_build", "obj_sanitized") if sanitize else OBJDIR
+    lib = SANITIZED_LIB if sanitize else LIB
+    extra = SANITIZE_FLAGS if sanitize else ()
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, objdir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
