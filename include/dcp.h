@@ -40,7 +40,8 @@ enum {
   DCP_ERR_INVALID_ARG = -1, /* a size, pointer or relation between arguments is wrong */
   DCP_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, head dims, layout) */
   DCP_ERR_WORKSPACE = -3,   /* workspace smaller than the size query returned */
-  DCP_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  DCP_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  DCP_ERR_SCRATCH = -5      /* the call needs more than the library's fixed scratch holds */
 };
 
 /* Element formats. DCP_FP8_E4M3 is the OCP 8-bit E4M3 format without
@@ -239,6 +240,40 @@ int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32
                             int32_t rank_count, float softmax_scale, int32_t algo,
                             float* out_o, float* out_lse, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch that dcp_partial_decode_attn_noalloc holds per
+ * device: enough for the 128-head, 512-dim MLA decode on a 256-CU device
+ * (its stream-K partials take about 129 MiB) and for the GQA kernels' far
+ * smaller plans. */
+#define DCP_NOALLOC_SCRATCH_BYTES ((size_t)136 << 20)
+
+/*
+ * dcp_partial_decode_attn_noalloc - dcp_partial_decode_attn for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same operation, arguments,
+ * kernels and results, with no workspace argument.
+ *
+ * The workspace is a static device array of DCP_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs this call on, from the first
+ * such call there until the process ends. The call allocates no device or
+ * pinned memory; it fails with DCP_ERR_SCRATCH when
+ * dcp_partial_decode_attn_workspace_size for the same arguments exceeds
+ * DCP_NOALLOC_SCRATCH_BYTES (nothing is launched then). The kernels write
+ * every scratch word they read within a call, so nothing carries over from
+ * the previous call. All calls on one device share that device's array:
+ * calls that may overlap there (on different streams, or from several host
+ * threads without ordering) race and must be serialised by the caller.
+ * Errors: those of dcp_partial_decode_attn except DCP_ERR_WORKSPACE, plus
+ * DCP_ERR_SCRATCH; DCP_ERR_HIP also when the scratch address cannot be
+ * obtained on the current device.
+ */
+int dcp_partial_decode_attn_noalloc(const void* q, int32_t q_dtype, int32_t batch,
+                                    int32_t num_q_heads, const dcp_kv_cache_t* kv,
+                                    const int32_t* block_table, int64_t block_table_stride,
+                                    int32_t max_vblocks, const int32_t* local_lens,
+                                    int32_t dcp_size, int32_t rank_begin, int32_t rank_count,
+                                    float softmax_scale, int32_t algo, float* out_o,
+                                    float* out_lse, void* stream);
 
 /*
  * dcp_partial_verify_attn - each rank's partial attention for several new

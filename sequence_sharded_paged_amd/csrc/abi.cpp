@@ -4,6 +4,7 @@
 #include <climits>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -154,6 +155,7 @@ const char* dcp_status_string(int status) {
     case DCP_ERR_UNSUPPORTED: return "unsupported dtype, geometry or layout";
     case DCP_ERR_WORKSPACE: return "workspace too small";
     case DCP_ERR_HIP: return "HIP runtime or launch error";
+    case DCP_ERR_SCRATCH: return "needs more than the library's fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -213,11 +215,37 @@ static size_t attn_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_he
   return workspace_for(p, k);
 }
 
+// Workspace of dcp_partial_decode_attn_noalloc, held by the library: one copy
+// per device, loaded with the library's code on that device. On the host the
+// array's name is only a stand-in for registration; kernels and copies get
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[DCP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchDevices];  // per device; static storage starts null
+
+// Address of the current device's scratch, looked up once per device.
+static int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DCP_ERR_HIP;
+  if (dev >= kScratchDevices) return DCP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DCP_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCP_OK;
+}
+
 static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q_len, int32_t num_q_heads,
                         const dcp_kv_cache_t* kv, const int32_t* block_table, int64_t block_table_stride,
                         int32_t max_vblocks, const int32_t* local_lens, int32_t dcp_size, int32_t rank_begin,
                         int32_t rank_count, float softmax_scale, int32_t algo, float* out_o, float* out_lse,
-                        void* workspace, size_t workspace_bytes, void* stream, bool profiled = true) {
+                        void* workspace, size_t workspace_bytes, void* stream, bool profiled = true,
+                        bool from_scratch = false) {
   AttnParams p{};
   AttnKernel k = AttnKernel::Generic;
   if (int st = validate_attn(batch, q_len, num_q_heads, q_dtype, kv, rank_count, algo, p, k)) return st;
@@ -228,6 +256,11 @@ static int partial_attn(const void* q, int32_t q_dtype, int32_t batch, int32_t q
   if (!q || !kv->k || !local_lens || !out_o || !out_lse) return DCP_ERR_INVALID_ARG;
   if (max_vblocks > 0 && !block_table) return DCP_ERR_INVALID_ARG;
   const size_t need = workspace_for(p, k);
+  if (from_scratch && need > 0) {  // the library's own workspace, after every other check
+    if (need > DCP_NOALLOC_SCRATCH_BYTES) return DCP_ERR_SCRATCH;
+    if (int st = scratch_of_current_device(&workspace)) return st;
+    workspace_bytes = DCP_NOALLOC_SCRATCH_BYTES;
+  }
   if (workspace_bytes < need || (need > 0 && !workspace)) return DCP_ERR_WORKSPACE;
   p.q = q;
   p.block_table = block_table;
@@ -327,6 +360,16 @@ int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32
   return partial_attn(q, q_dtype, batch, 1, num_q_heads, kv, block_table, block_table_stride, max_vblocks,
                       local_lens, dcp_size, rank_begin, rank_count, softmax_scale, algo, out_o, out_lse, workspace,
                       workspace_bytes, stream);
+}
+
+int dcp_partial_decode_attn_noalloc(const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                                    const dcp_kv_cache_t* kv, const int32_t* block_table,
+                                    int64_t block_table_stride, int32_t max_vblocks, const int32_t* local_lens,
+                                    int32_t dcp_size, int32_t rank_begin, int32_t rank_count, float softmax_scale,
+                                    int32_t algo, float* out_o, float* out_lse, void* stream) {
+  return partial_attn(q, q_dtype, batch, 1, num_q_heads, kv, block_table, block_table_stride, max_vblocks,
+                      local_lens, dcp_size, rank_begin, rank_count, softmax_scale, algo, out_o, out_lse, nullptr, 0,
+                      stream, false, true);
 }
 
 size_t dcp_partial_verify_attn_workspace_size(int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t q_dtype,

@@ -14,7 +14,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DCP_LIB", os.path.join(_HERE, "lib", "libdcp.so"))
 
-DCP_OK, DCP_ERR_INVALID_ARG, DCP_ERR_UNSUPPORTED, DCP_ERR_WORKSPACE, DCP_ERR_HIP = 0, -1, -2, -3, -4
+DCP_OK, DCP_ERR_INVALID_ARG, DCP_ERR_UNSUPPORTED, DCP_ERR_WORKSPACE, DCP_ERR_HIP, DCP_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+DCP_NOALLOC_SCRATCH_BYTES = 136 << 20
 DCP_F32, DCP_BF16, DCP_FP8_E4M3 = 0, 1, 2
 DCP_ALGO_AUTO, DCP_ALGO_GENERIC, DCP_ALGO_FAST = 0, 1, 2
 
@@ -25,7 +26,7 @@ EXPORTS = [
     "dcp_partial_decode_attn_workspace_size", "dcp_partial_decode_attn", "dcp_lse_merge",
     "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
     "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn", "dcp_gather_context",
-    "dcp_profile_enable", "dcp_profile_collect", "dcp_check_block_table",
+    "dcp_profile_enable", "dcp_profile_collect", "dcp_check_block_table", "dcp_partial_decode_attn_noalloc",
 ]
 
 
@@ -72,6 +73,9 @@ def lib():
         L.dcp_partial_decode_attn.restype = ctypes.c_int
         L.dcp_partial_decode_attn.argtypes = [vp, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp, i32,
                                               i32, i32, f32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dcp_partial_decode_attn_noalloc.restype = ctypes.c_int
+        L.dcp_partial_decode_attn_noalloc.argtypes = [vp, i32, i32, i32, ctypes.POINTER(KvCache), vp, i64, i32, vp,
+                                                      i32, i32, i32, f32, i32, vp, vp, vp]
         L.dcp_lse_merge.restype = ctypes.c_int
         L.dcp_lse_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp]
         L.dcp_partial_verify_attn_workspace_size.restype = ctypes.c_size_t
@@ -197,6 +201,22 @@ def dcp_partial_decode_attn(q, kv: KvCache, block_table, local_lens, dcp_size, r
         _ptr(q), TORCH_TO_DCP[q.dtype], B, Hq, ctypes.byref(kv), _ptr(block_table), block_table.stride(0),
         max_vblocks, _ptr(local_lens), dcp_size, rank_begin, rank_count, float(softmax_scale), algo,
         _ptr(out_o), _ptr(out_lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dcp_partial_decode_attn_noalloc(q, kv: KvCache, block_table, local_lens, dcp_size, rank_begin, rank_count,
+                                    softmax_scale, out_o, out_lse, algo=DCP_ALGO_AUTO, max_vblocks=None, stream=None):
+    """``dcp_partial_decode_attn`` with the library's fixed device scratch as
+    its workspace (no workspace argument, no device allocation)."""
+    B, Hq, _ = q.shape
+    assert q.is_contiguous() and local_lens.dtype == torch.int32 and local_lens.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.stride(1) == 1
+    assert out_o.dtype == torch.float32 and out_lse.dtype == torch.float32
+    if max_vblocks is None:
+        max_vblocks = block_table.shape[1]
+    _check("dcp_partial_decode_attn_noalloc", lib().dcp_partial_decode_attn_noalloc(
+        _ptr(q), TORCH_TO_DCP[q.dtype], B, Hq, ctypes.byref(kv), _ptr(block_table), block_table.stride(0),
+        max_vblocks, _ptr(local_lens), dcp_size, rank_begin, rank_count, float(softmax_scale), algo,
+        _ptr(out_o), _ptr(out_lse), _stream(stream)))
 
 
 def dcp_partial_verify_attn_workspace_size(batch, q_len, num_q_heads, q_dtype, kv: KvCache, rank_count,

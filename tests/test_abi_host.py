@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert native.dcp_abi_version() == 1
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert native.status_string(st) not in ("", "unknown status")
     assert native.status_string(-99) == "unknown status"
 
@@ -268,3 +268,29 @@ def test_product_path_loads_no_oracle():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_noalloc_validation(L):
+    """The no-allocation decode entry point checks its arguments like the one
+    with a workspace, then refuses (before looking up its scratch or launching
+    anything) a problem whose workspace exceeds the fixed scratch."""
+    p = _fake(64)
+    f = L.dcp_partial_decode_attn_noalloc
+
+    def call(kv, batch=4, hq=8, bt_stride=4, max_vb=4, dcp=4, rb=0, rc=2, scale=0.1, q=p, algo=0):
+        return f(q, native.DCP_BF16, batch, hq, ctypes.byref(kv), p, bt_stride, max_vb, p, dcp, rb, rc,
+                 ctypes.c_float(scale), algo, p, p, NULL)
+
+    kv = _kv()
+    assert call(kv, rb=3, rc=2) == INV
+    assert call(kv, bt_stride=2) == INV
+    assert call(kv, scale=float("nan")) == INV
+    assert call(kv, q=NULL) == INV
+    assert call(kv, hq=7) == INV
+    assert call(kv, batch=0) == 0                  # empty: nothing launched, no scratch needed
+    mla = _kv(num_kv_heads=1, head_dim_k=576, head_dim_v=512, v=None)
+    st, n = _ws(L, mla, batch=1 << 20, hq=128, rc=8)
+    assert st == 0 and n > native.DCP_NOALLOC_SCRATCH_BYTES
+    assert call(mla, batch=1 << 20, hq=128, dcp=8, rc=8) == native.DCP_ERR_SCRATCH
+    st, n = _ws(L, mla, batch=64, hq=128, rc=8)    # the bimodal MLA batch fits
+    assert st == 0 and 0 < n <= native.DCP_NOALLOC_SCRATCH_BYTES
