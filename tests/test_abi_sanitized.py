@@ -3,8 +3,7 @@
 (device code unchanged) and the host ABI checks of test_abi_host.py run
 against it in a child process with the ASan runtime preloaded. An overflow,
 use after free or undefined behaviour in argument validation, the workspace
-size queries or descriptor handling
-aborts the child and fails this test."""
+size queries or descriptor handling aborts the child and fails this test."""
 
 import glob
 import os
