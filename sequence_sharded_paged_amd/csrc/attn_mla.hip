@@ -9,45 +9,58 @@
 // against the local KV shard, partial output and LSE out).
 //
 // At 128 heads a token costs 2 x 128 x (576 + 512) flops for 1152 bytes, so
-// at the HBM rate this kernel needs most of the chip's bf16 MFMA rate: the
-// design goal is to keep the matrix cores busy, and everything else (LDS
-// operand reads, softmax, address arithmetic) runs in their shadow.
+// at the HBM rate this kernel needs most of the chip's bf16 MFMA rate. The
+// design keeps the matrix cores fed from LDS at a rate one wavefront can
+// sustain: on gfx950 the LDS serves a CU about 220 B/clk, but a single
+// wavefront draws only about 29 B/clk from it, so with one wavefront per SIMD
+// an MFMA that needs a fresh 1 KB LDS operand every 32 cycles (the previous
+// design's score phase) waits on the LDS.
 //
 // Work split: stream-K over (rank, request, query token) units (splitkv.h;
 // one query token per unit when several are decoded at once), one persistent
-// 256-thread workgroup (one wavefront per SIMD) per worker, tiles of 32
-// tokens. Per workgroup:
-//   * a 4-stage LDS ring of 32-token tiles (36 KB each) is filled straight
-//     from HBM with global_load_lds_dwordx4 (each wavefront loads 8 of the 32
-//     rows); the 16-byte chunks of a row are XOR-swizzled by the row index so
-//     that the MFMA operand reads spread over the LDS banks. At any time two
-//     stages are read (scores of tile t, values of tile t - 1) and two are in
-//     flight (the refill with tile t + 2 goes out during step t);
-//   * scores: wavefront w owns query heads 32 w .. 32 w + 31, whose Q (32 x
-//     576 bf16, 144 VGPRs) stays in registers for the whole piece;
-//     S^T[token, head] = K[token, :] . Q[head, :] on 32x32x16 bf16 MFMA, K
-//     rows read from LDS with ds_read_b128;
-//   * softmax weights in log2 units relative to a per-piece reference max
-//     (the first tile's): no rescaling of the accumulator and no cross-lane
-//     reduction inside the loop; a piece whose scores outgrow the reference
-//     by more than 2^64 is replayed with a higher reference. The weights are
-//     rounded to bf16 for the value product and their sum (the normaliser) is
-//     taken over the same rounded values, with an fp32 sum of the unrounded
-//     weights for the LSE (as in the GQA kernel);
-//   * values: the weights of all 128 heads go through an 8 KB LDS buffer, and
+// 256-thread workgroup (one wavefront per SIMD) per CU, tiles of 16 tokens.
+// Per workgroup and tile:
+//   * the tile (16 rows x 1152 B) sits in a 7-stage LDS ring, filled straight
+//     from HBM with global_load_lds_dwordx4, in score-operand order: 18
+//     blocks of 1 KB, block ks holding dims 32 ks .. 32 ks + 31 of every row,
+//     16-byte chunk c of row t at slot 16 c + (t ^ 4 c) (the XOR keeps the
+//     transposing value-operand reads free of bank conflicts). Tiles are
+//     loaded five ahead, so a tile has about three steps to arrive;
+//   * scores: the wavefront pair (0, 1) handles heads 0..63, the pair (2, 3)
+//     heads 64..127; within a pair, wavefront dh takes key dims 288 dh ..
+//     288 dh + 287. Each wavefront holds Q for its 64 heads x 288 dims (144
+//     VGPRs) and computes partial scores S^T[token, head] on 16x16x32 bf16
+//     MFMAs: every K operand read from LDS feeds four MFMAs (four head
+//     tiles), a quarter of the LDS traffic per MFMA of a one-head-tile
+//     layout;
+//   * the pair exchanges partial scores through LDS (2 KB per wavefront per
+//     tile): wavefront dh keeps heads 32 dh .. 32 dh + 31 of its pair's 64,
+//     adds the partner's partial and owns their softmax;
+//   * softmax in log2 units relative to a per-piece reference max (the first
+//     tile's): no rescaling of the accumulators and no cross-lane reduction
+//     inside the loop; a piece whose scores outgrow the reference by more
+//     than 2^64 is replayed with a higher reference. Weights are rounded to
+//     bf16 for the value product and their sum (the normaliser) is taken over
+//     the same rounded values, with an fp32 sum of the unrounded weights for
+//     the LSE. Tokens past the shard's end are masked after scaling, so any
+//     finite softmax scale (zero and negative included) is handled;
+//   * values: the bf16 weights of all 128 heads go through a 4 KB LDS buffer;
 //     wavefront w owns latent dims 128 w .. 128 w + 127 of every head:
-//     O^T[dim, head] += V^T[dim, token] . P^T[token, head], its O (128 x 128
-//     fp32, 256 AGPRs) in registers for the whole piece. V^T comes from the
-//     tile's LDS rows through ds_read_b64_tr_b16, whose 16-lane transpose
-//     hands each lane four consecutive tokens of one dimension. Splitting the
-//     value product by dimension rather than by head means each wavefront
-//     reads a quarter of the V tile: the transposing reads move half the bytes
-//     per instruction of ds_read_b128, and when every wavefront read the whole
-//     V tile they were the largest LDS cost of the kernel;
-//   * software pipeline across tiles: step t runs the score MFMAs of tile t,
-//     then the value MFMAs of tile t - 1 with the softmax of tile t
-//     interleaved (two weights per value step), then stores tile t's weights;
-//     one barrier per step publishes them and the refill that landed.
+//     O^T[dim, head] += V^T[dim, token] . P^T[token, head] on 32x32x16 bf16
+//     MFMAs, its O (128 x 128 fp32) in AGPRs for the whole piece. V^T comes
+//     from the tile's LDS rows through ds_read_b64_tr_b16 (a 16-lane
+//     transpose handing each lane four consecutive tokens of one dim);
+//   * software pipeline, one workgroup barrier per tile: after the barrier
+//     that publishes tile t's partial scores, step t issues the DMA of tile
+//     t + 5 and runs one MFMA stream that interleaves the score MFMAs of tile
+//     t + 1 with the value MFMAs of tile t - 1 (independent accumulators, so
+//     neither waits on its own accumulation chain), with the softmax of tile t
+//     in its shadow; it then stores tile t's weights and sends tile t + 1's
+//     partial scores.
+//
+// DMA sources come from a scalar walker over the worker's tiles (a few scalar
+// instructions per tile); block-table entries are read through a 64-entry
+// window held one per lane of a VGPR and refilled once per 64 blocks or unit.
 #include <utility>
 
 #include "splitkv.h"
@@ -57,39 +70,32 @@ namespace dcp {
 constexpr int kMlaDk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaHeads = 128;
-constexpr int kMlaTile = 32;                                     // tokens per tile
-constexpr int kMlaStages = 4;                                    // LDS ring depth
-constexpr int kMlaRowBytes = kMlaDk * 2;                         // 1152
-constexpr int kMlaStageBytes = kMlaTile * kMlaRowBytes;          // 36864
-constexpr int kMlaLatBytes = kMlaDv * 2;                         // 1024: latent part of a row (also V)
-constexpr int kMlaRopeOff = kMlaTile * kMlaLatBytes;             // 32768: rope rows follow the latent rows
-constexpr int kMlaRopeBytes = kMlaRowBytes - kMlaLatBytes;       // 128
-constexpr int kMlaWaves = 4;                                     // wavefronts per workgroup
+constexpr int kMlaTile = 16;                                   // tokens per tile
+constexpr int kMlaStages = 7;                                  // LDS ring depth
+constexpr int kMlaAhead = 5;                                   // tiles loaded ahead of the scores
+constexpr int kMlaRowBytes = kMlaDk * 2;                       // 1152
+constexpr int kMlaBlocks = kMlaDk / 32;                        // 18 operand blocks of 1 KB per tile
+constexpr int kMlaStageBytes = kMlaBlocks * 1024;              // 18432
+constexpr int kMlaWaves = 4;
 constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kMlaHeadsPerWave = kMlaHeads / kMlaWaves;          // 32: the N side of the MFMAs
-constexpr int kMlaRowsPerWave = kMlaTile / kMlaWaves;            // 8 rows of a tile loaded per wavefront
-constexpr int kMlaDmaPerTile = kMlaRowsPerWave + 1;              // DMA instructions per wavefront and tile
-constexpr int kMlaKSteps = kMlaDk / 16;                          // 36 score k-steps of 16 dims
-constexpr int kMlaKStepsLat = kMlaDv / 16;                       // 32 latent k-steps (Q in VGPRs)
-constexpr int kMlaDvTiles = kMlaDv / 32 / kMlaWaves;             // 4 value M-tiles of 32 dims per wave
-constexpr int kMlaHeadTiles = kMlaHeads / 32;                    // 4 value N-tiles of 32 heads
-constexpr int kMlaValSteps = 2 * kMlaDvTiles;                    // (token step, M-tile) pairs per tile
-constexpr int kMlaPBytes = kMlaTile * kMlaHeads * 2;             // 8 KB of bf16 weights per tile
-#ifndef DCP_MLA_KPF
-#define DCP_MLA_KPF 4
+constexpr int kMlaKSteps = kMlaBlocks / 2;                     // 9 score k-steps (32 dims) per wavefront
+constexpr int kMlaDvTiles = kMlaDv / 32 / kMlaWaves;           // 4 value M-tiles of 32 dims per wavefront
+constexpr int kMlaHeadTiles = kMlaHeads / 32;                  // 4 value N-tiles of 32 heads
+constexpr int kMlaPBytes = kMlaTile * kMlaHeads * 2;           // 4 KB of bf16 weights per tile
+constexpr int kMlaXBytes = kMlaWaves * 2048;                   // partial scores sent per tile
+#ifndef DCP_MLA_KAHEAD
+#define DCP_MLA_KAHEAD 1
 #endif
-#ifndef DCP_MLA_VPF
-#define DCP_MLA_VPF 2
-#endif
-constexpr int kMlaKPf = DCP_MLA_KPF;  // score-operand read distance (k-steps)
-constexpr int kMlaVPf = DCP_MLA_VPF;  // value-operand read distance (value steps)
+constexpr int kMlaKAhead = DCP_MLA_KAHEAD;                    // score operand read distance (k-steps)
 constexpr int kMlaMaxWorkers = 512;
 constexpr float kMlaRefSlack = 64.f;  // log2 units a score may exceed the piece's reference
 
-static_assert(kMlaStages == 4, "the refill distance below assumes 4 stages");
-static_assert(kMlaKStepsLat == 32 && kMlaKSteps - kMlaKStepsLat == 4, "32 latent + 4 rope k-steps");
+static_assert(kMlaStages >= kMlaAhead + 2, "the refill of tile t + ahead goes to the stage of tile t - 2");
+static_assert(kMlaStages * kMlaStageBytes + 2 * kMlaPBytes + 2 * kMlaXBytes + 2048 <= 160 * 1024, "LDS");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order
 template <typename F, int... I>
@@ -100,7 +106,6 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Uniform read-only load through the constant address space (scalar load).
 template <typename T>
@@ -115,33 +120,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (the wave's
-// M0 base). Issued through asm so that the compiler, which cannot tell the
-// ring stages apart, does not make every later LDS read wait for it; the
-// kernel orders these writes itself (vmcnt wait + barrier before a stage is
-// read, barrier before it is refilled).
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  // one wait state between the M0 write and the LDS DMA that reads it
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Same, from a wave-uniform base plus a 32-bit per-lane byte offset.
-// (The base and M0 values are wave-uniform by construction; readfirstlane
-// pins them to SGPRs where the compiler cannot prove it.) The asm only moves
-// into M0: any SALU arithmetic here would overwrite SCC, which the compiler
-// may hold live across the statement.
-__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  // (readfirstlane yields a signed int: each half is taken as uint32_t before
-  // widening, or a low word with bit 31 set would smear into the high word)
-  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
-  const uint64_t bu = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(reinterpret_cast<const void*>(bu)), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
+// s_waitcnt lgkmcnt(0) with vmcnt / expcnt left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every tile in flight); the asm memory clobber keeps the compiler
@@ -152,294 +132,224 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
 }
 
-
-// s_waitcnt lgkmcnt(0) with vmcnt / expcnt left alone.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-
-// bf16 pair (round to nearest even) packed in one dword, low half first.
-__device__ __forceinline__ bf16x2_t pack_bf16(float lo, float hi) {
-  return bf16x2_t{static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+// 16 bytes per lane from sbase + voff + kImm into LDS at lds_base + 16 * lane.
+// The instruction's immediate offset applies to both addresses (global and
+// LDS), so M0 is set to lds_base - kImm.
+// Issued through asm so that the compiler, which cannot tell the ring stages
+// apart, does not make later LDS reads wait for it; the kernel orders these
+// writes itself (vmcnt wait + barrier before a stage is read, barrier before it
+// is refilled). The base and M0 values are wave-uniform by construction
+// (readfirstlane pins them to SGPRs); the asm only moves into M0, since SALU
+// arithmetic inside it would overwrite SCC, which the compiler may hold live.
+template <int kImm>
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  static_assert(kImm >= 0 && kImm < 4096, "global offset immediate");
+  // (readfirstlane yields a signed int: each half is taken as uint32_t before
+  // widening, or a low word with bit 31 set would smear into the high word)
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  const uint64_t bu = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(bu)), "s"(__builtin_amdgcn_readfirstlane(lds_base - kImm)), "i"(kImm)
+               : "memory", "m0");
 }
 
-// LDS tile layout, in MFMA operand order. The tile's 32 rows x 72 chunks of
-// 16 bytes form 36 blocks of 1 KB, block 2 ks + u holding chunks 4 ks .. 4 ks
-// + 3 of rows 16 u .. 16 u + 15 (the score operand of k-step ks for token
-// half u): chunk 4 ks + c of row 16 u + r sits at 16 (16 c + (r ^ 4 c)) in
-// its block. A score-operand read (lane 16 c + r) is then one contiguous
-// 1 KB block, and a transpose read of the value operand (4 rows x 2 chunks
-// per 16 lanes) touches two 64-byte runs in different bank halves.
-__device__ __forceinline__ int mla_slot(int r, int c) { return 16 * c + (r ^ (4 * c)); }
+// Slot (16-byte unit) of chunk c (0..3) of row t (0..15) inside a 1 KB block.
+__device__ __forceinline__ int mla_slot(int t, int c) { return 16 * c + (t ^ (4 * c)); }
 
-__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads), amdgpu_waves_per_eu(1, 1)))
-mla_attn_kernel(AttnParams p, int workers) {
-  __shared__ __attribute__((aligned(16))) char lds[kMlaStages * kMlaStageBytes];
-  // bf16 weights of tile t in buffer t % 2, in value-operand order: the 1 KB
-  // block 2 nt + kk holds, at 16 l, head 32 nt + l % 32, tokens 16 kk + 8 (l /
-  // 32) .. +7 (lane l's part of the B operand of N-tile nt, token step kk).
-  // Wave w writes blocks 2 w, 2 w + 1 (its own heads).
-  __shared__ __attribute__((aligned(16))) char pbuf[2 * kMlaPBytes];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int n = lane & 15, g = lane >> 4;
+// O += A . B on a 32x32x16 bf16 MFMA, a compiler builtin: the compiler then
+// tracks the wait states of every other instruction that reads or moves O,
+// including the copies it makes between code paths.
+__device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+// Score MFMA (16x16x32 bf16) with its accumulator in VGPRs, issued through
+// asm: with the AGPRs full of O accumulators the compiler would give a
+// builtin score MFMA an AGPR destination and move an O tile out of its way
+// around every step. The first k-step starts from the constant 0, the
+// following ones accumulate in place; score_settle() then provides the wait
+// states (an MFMA of n passes needs about n + 3 before another instruction
+// reads its destination; this one takes 4) and names the scores as operands,
+// so that no read of them is scheduled above it. The first form's result is
+// early-clobber: an MFMA's destination must not overlap its A or B operand.
+__device__ __forceinline__ void mfma_score_first(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_score(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void score_settle(f32x4_t (&s)[4]) {
+  asm volatile("s_nop 15" : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3]));
+}
+
+struct MlaShared {
+  char* ring;    // kMlaStages x kMlaStageBytes
+  char* pbuf;    // 2 x kMlaPBytes: bf16 weights of tile t in buffer t % 2
+  char* xbuf;    // 2 x kMlaXBytes: partial scores of tile t in buffer t % 2
+  float* s_norm;  // [128]: normaliser of each head, exchanged at a piece's end
+  int* s_vote;    // [4]: replay votes
+};
+
+// The tile walker that feeds the DMAs (identical and wave-uniform in every
+// wavefront): tiles in order from the worker's first, each giving the address
+// of its first row and how many of its 16 rows are inside the shard.
+struct MlaWalker {
+  int t;           // next tile, relative to the worker's first tile
+  int last;        // the worker's last tile (relative): later requests repeat it
+  int u;           // unit of tile t
+  int uend;        // end of unit u (relative tile index, clamped to the int range)
+  int tok, len;    // first token of tile t in the unit's shard, shard length
+  int vb, off;     // block-table column and in-block token offset of tile t
+  int win_lo;      // the window holds columns win_lo .. win_lo + 63 (-1: none)
+  int win;         // this lane's column win_lo + lane
+  const int32_t* bt;
+  const char* rank_base;
+  const char* blk_base;  // base of block vb in the unit's rank pool
+  const char* addr;      // first row of the last tile produced
+  int nv;                // valid rows of the last tile produced
+};
+
+template <int DH>
+__device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared& sh, int workers, const SplitWs& ws,
+                                           int64_t wstart, int64_t wend) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
+  const int hg = wave >> 1;                                          // head group: heads 64 hg .. 64 hg + 63
   const int worker = blockIdx.x;
-  const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, workers);
-  const int64_t T = ld_uniform(ws.prefix + U);
-  if (T == 0 || worker >= workers) return;
-  const int64_t tpw = (T + workers - 1) / workers;
-  const int64_t wstart = static_cast<int64_t>(worker) * tpw;
-  if (wstart >= T) return;
-  const int64_t wend = min(T, wstart + tpw);
+  const int g4 = lane >> 4, n16 = lane & 15;
 
   const int bs = p.kv.block_size;
   const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks3 = p.kv.k_stride[3];
-  const int row_bytes = static_cast<int>(ks3 * 2);  // bytes between consecutive tokens of a block
+  const int row_bytes = static_cast<int>(ks3 * 2);
+  const uint64_t blk_bytes = static_cast<uint64_t>(ks1) * 2;
   const char* kbase = static_cast<const char*>(p.kv.k);
-  // The kernel masks a shard's tail tokens with -inf scores before scaling,
-  // which needs a positive scale: a negative one is carried by Q's sign bits
-  // (s c2 = (-s) (-c2), exact in bf16), a zero one by a zeroed Q and scale 1
-  // (every weight is then exp2(0 - m_ref), as with scale 0).
-  const float c2_in = p.softmax_scale * DCP_LOG2E;
-  const float c2 = c2_in > 0.f ? c2_in : (c2_in < 0.f ? -c2_in : 1.f);
-  const uint32_t q_keep = c2_in == 0.f ? 0u : 0xFFFFFFFFu, q_flip = c2_in < 0.f ? 0x80008000u : 0u;
-  const uint32_t lds0 = lds_addr(lds);
+  const float c2 = p.softmax_scale * DCP_LOG2E;
+  const uint32_t ring0 = lds_addr(sh.ring);
   auto stage_of = [&](int64_t t) __attribute__((always_inline)) {
-    return static_cast<int>((t - wstart) & (kMlaStages - 1));
+    return static_cast<int>(static_cast<uint32_t>(t - wstart) % kMlaStages);  // tiles per worker < 2^31
   };
 
-  // ---- tile sources -----------------------------------------------------------
-  // A walker over the worker's tiles in order, yielding this wave's refill
-  // (its 16-token half of the tile: tokens t0 + 16 (w % 2) .. +15, which share
-  // one block, block_size % 16 == 0). Per unit it caches the length,
-  // block-table row and rank base; per tile it advances the (virtual block,
-  // offset) of the tile's first token. Rows past the shard's end are replaced
-  // by the last valid row of the half, or of the first half if the second has
-  // none (finite data, zero weight).
-  //
-  // Block-table entries come from a window of 64 consecutive entries of the
-  // unit's row, one per lane of a VGPR, read with v_readlane: a scalar load
-  // per block would stall the loop for a cache miss (the KV stream keeps the
-  // table out of the caches) and, sharing a counter with the LDS reads, drain
-  // them; the window is reloaded once per 64 blocks. Tile indices are kept
-  // relative to the worker's first tile, in 32 bits, and the per-tile work
-  // is a few scalar instructions: with one wavefront per SIMD every
-  // instruction of the loop costs an issue slot.
-  const int my_half = wave & 1;
-  const int dma_row = n ^ (4 * g);
-  const uint32_t blk_bytes = static_cast<uint32_t>(ks1 * 2);  // < 2^32 (checked on the host)
-  const uint32_t voff_full = static_cast<uint32_t>(dma_row * row_bytes + 16 * g + 64 * (wave >> 1));
-  const uint32_t m0_wave = lds0 + wave * 1024;
-  struct Walker {
-    int t;     // next tile, relative to wstart
-    int u;     // its unit
-    int uend;  // end of unit u, relative to wstart (clamped to the int range)
-    int tok;   // first token of tile t within the unit's shard
-    int len;
-    int hvb, hoff;     // block and offset of token tok + 16 (w % 2), this wave's half
-    bool dirty;        // hbase must be recomputed (new unit or new block)
-    const char* hbase; // address of that token's row
-    int win, win_lo;   // entries win_lo + lane of the row (win_lo < 0: no window)
-    const int32_t* bt;
-    const char* rk;
-  };
-  struct Refill {
-    const char* base;  // this wave's token half
-    uint32_t voff;     // lane offset of k-step w / 2
-    uint32_t m0;       // LDS address of block w of the stage
-  };
+  // ---- DMA walker ------------------------------------------------------------------
+  // DMA blocks of this wavefront: 2 DH + hg + 4 k (k < kDma): wavefronts with
+  // DH = 0 load five of the 18 blocks, DH = 1 four.
+  constexpr int kDma = DH == 0 ? 5 : 4;
+  const int dma_first = 2 * DH + hg;
+  // lane l = 16 c + u fetches row u ^ 4 c, chunk c of each block (slot l)
+  const int dma_row = n16 ^ (4 * g4);
+  const uint32_t dma_col = static_cast<uint32_t>(16 * g4 + 64 * hg);
   auto rel_end = [&](int64_t e) __attribute__((always_inline)) {
     return static_cast<int>(min(e - wstart, static_cast<int64_t>(INT32_MAX)));
   };
-  // (re)enter unit w.u at tile w.t, the unit starting at tile ubeg (absolute)
-  auto set_unit = [&](Walker& w, int64_t ubeg) __attribute__((always_inline)) {
-    // unit u = (r * batch + b) * q_len + i: rank r, request b, query token i
-    const int rb = w.u / p.q_len, i = w.u - rb * p.q_len;
-    const int b = rb % p.batch, r = rb / p.batch;
-    w.len = ld_uniform(p.local_lens + (static_cast<int64_t>(b) * p.q_len + i) * p.dcp_size + p.rank_begin + r);
-    w.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
-    w.rk = kbase + r * ks0 * 2;
-    w.tok = static_cast<int>(wstart + w.t - ubeg) * kMlaTile;
-    const int ht = w.tok + 16 * my_half;
-    w.hvb = ht / bs;
-    w.hoff = ht - w.hvb * bs;
-    w.dirty = true;
-    w.win_lo = -1;
+  MlaWalker dw;
+  auto win_load = [&](int vb) __attribute__((always_inline)) {
+    dw.win_lo = vb;
+    dw.win = vb + lane < p.max_vblocks ? dw.bt[vb + lane] : 0;
+    wait_vmcnt<0>();  // the window is needed now (rare: per unit or per 64 blocks)
   };
-  // a walker at tile t, searching forward from unit u (at or before t's unit)
-  auto walker_at = [&](int64_t t, int64_t u) __attribute__((always_inline)) {
-    Walker w;
+  auto set_block = [&]() __attribute__((always_inline)) {
+    if (dw.vb - dw.win_lo >= 64 || dw.win_lo < 0) win_load(dw.vb);  // uniform
+    const uint32_t blk = static_cast<uint32_t>(__builtin_amdgcn_readlane(dw.win, dw.vb - dw.win_lo));
+    dw.blk_base = dw.rank_base + static_cast<uint64_t>(blk) * blk_bytes;
+  };
+  // enter unit u at relative tile dw.t (the unit spans tiles [ubeg, uend))
+  auto set_unit = [&](int u, int64_t ubeg, int64_t uend) __attribute__((always_inline)) {
+    dw.u = u;
+    dw.uend = rel_end(uend);
+    const int rb = u / p.q_len, qi = u - rb * p.q_len;
+    const int b = rb % p.batch, r = rb / p.batch;
+    dw.len = ld_uniform(p.local_lens + (static_cast<int64_t>(b) * p.q_len + qi) * p.dcp_size + p.rank_begin + r);
+    dw.bt = p.block_table + static_cast<int64_t>(b) * p.bt_stride;
+    dw.rank_base = kbase + static_cast<int64_t>(r) * ks0 * 2;
+    dw.tok = static_cast<int>(wstart + dw.t - ubeg) * kMlaTile;
+    dw.vb = dw.tok / bs;
+    dw.off = dw.tok - dw.vb * bs;
+    dw.win_lo = -1;
+    set_block();
+  };
+  // position the walker at relative tile t, searching units forward from u
+  auto walker_at = [&](int t, int64_t u) __attribute__((always_inline)) {
     int64_t ubeg = ld_uniform(ws.prefix + u), uend = ld_uniform(ws.prefix + u + 1);
-    while (uend <= t) {  // uniform
+    while (uend <= wstart + t) {  // uniform
       ++u;
       ubeg = uend;
       uend = ld_uniform(ws.prefix + u + 1);
     }
-    w.t = static_cast<int>(t - wstart);
-    w.u = static_cast<int>(u);
-    w.uend = rel_end(uend);
-    w.win = 0;
-    w.hbase = kbase;
-    set_unit(w, ubeg);
-    return w;
+    dw.t = t;
+    dw.last = static_cast<int>(wend - 1 - wstart);
+    set_unit(static_cast<int>(u), ubeg, uend);
   };
-  // block-table entry vb (< max_vblocks) of the walker's row
-  auto entry = [&](Walker& w, int vb) __attribute__((always_inline)) {
-    if (w.win_lo < 0 || vb < w.win_lo || vb >= w.win_lo + 64) {  // uniform
-      w.win_lo = vb;
-      w.win = vb + lane < p.max_vblocks ? w.bt[vb + lane] : 0;
-      // wait here, on the reload path only (the compiler does not see the ring's
-      // DMAs and would otherwise put a full wait where the paths join)
-      wait_vmcnt<0>();
-    }
-    return __builtin_amdgcn_readlane(w.win, vb - w.win_lo);
-  };
-  auto row_at = [&](Walker& w, int vb, int off) __attribute__((always_inline)) {
-    const uint32_t blk = static_cast<uint32_t>(entry(w, vb));
-    return w.rk + static_cast<uint64_t>(blk) * blk_bytes + static_cast<uint32_t>(off * row_bytes);
-  };
-  // The refill of the DMA walker's next tile (stage t % 4); advances it. The
-  // common case (same unit, same block, a whole half) adds 32 rows to the
-  // half's address.
-  Walker dw;
-  auto prepare = [&]() __attribute__((always_inline)) {
-    Walker& w = dw;
-    if (w.t >= w.uend) {  // uniform, rare: the tile opens the next non-empty unit
-      int64_t ubeg = wstart + w.uend, uend;
+  // The walker's next tile (the last tile again once the worker's run out).
+  auto next_tile = [&]() __attribute__((always_inline)) {
+    if (dw.t > dw.last) return;  // uniform: keep the last tile's addr / nv
+    if (dw.t >= dw.uend) {       // uniform, rare: the next non-empty unit
+      int64_t ubeg = wstart + dw.uend, uend;
+      int u = dw.u;
       for (;;) {
-        ++w.u;
-        uend = ld_uniform(ws.prefix + w.u + 1);
+        ++u;
+        uend = ld_uniform(ws.prefix + u + 1);
         if (uend > ubeg) break;
       }
-      w.uend = rel_end(uend);
-      set_unit(w, ubeg);
+      set_unit(u, ubeg, uend);
     }
-    if (w.dirty) {  // uniform
-      w.hbase = row_at(w, w.hvb, w.hoff);
-      w.dirty = false;
+    dw.addr = dw.blk_base + static_cast<uint32_t>(dw.off * row_bytes);
+    dw.nv = min(kMlaTile, dw.len - dw.tok);
+    ++dw.t;
+    dw.tok += kMlaTile;
+    dw.off += kMlaTile;
+    if (dw.off == bs && dw.t <= dw.last && dw.t < dw.uend) {  // uniform: the next tile opens a block
+      dw.off = 0;
+      ++dw.vb;
+      set_block();
     }
-    Refill r;
-    r.base = w.hbase;
-    r.voff = voff_full;
-    r.m0 = m0_wave + (w.t & (kMlaStages - 1)) * kMlaStageBytes;
-    const int nv = w.len - w.tok - 16 * my_half;  // valid rows of the half (if < 16)
-    if (nv < 16) {  // uniform, rare: the unit's last tile
-      int rows = nv;
-      if (nv <= 0) {  // no second half: take the first half's rows
-        rows = min(16, w.len - w.tok);
-        const int fvb = w.tok / bs;
-        r.base = row_at(w, fvb, w.tok - fvb * bs);
-      }
-      r.voff = static_cast<uint32_t>(min(dma_row, rows - 1) * row_bytes + 16 * g + 64 * (wave >> 1));
-    }
-    ++w.t;
-    w.tok += kMlaTile;
-    w.hoff += kMlaTile;
-    if (w.hoff < bs) {  // uniform
-      w.hbase += kMlaTile * row_bytes;
-    } else {
-      do {  // once, or twice when block_size is 16
-        w.hoff -= bs;
-        ++w.hvb;
-      } while (w.hoff >= bs);
-      w.dirty = true;
-    }
-    return r;
   };
-
-  // ---- DMA producer -------------------------------------------------------------
-  // Wave w loads blocks w, w+4, .., w+32 of each tile: token half w % 2,
-  // k-steps w / 2 + 2 k (k = 0 .. 8); DMA lane 16 c + m fetches row m ^ 4 c of
-  // the half, chunk 4 ks + c. A refill (one wave's share of a tile) is
-  // prepared at the end of a step and its 9 DMAs are spread over the k-steps
-  // of the next score phase.
-  // DMA k (0 .. 8) of this wave for the refill r: k-step w / 2 + 2 k, block w + 4 k
-  auto dma = [&](const Refill& r, auto kc) __attribute__((always_inline)) {
-    constexpr int k = decltype(kc)::value;
-    dma16_s(r.voff + 128 * k, r.base, r.m0 + 4096 * k);
+  // DMAs of the walker's next tile into stage s
+  auto dma_tile = [&](int s) __attribute__((always_inline)) {
+    next_tile();
+    const uint32_t voff = static_cast<uint32_t>(min(dma_row, dw.nv - 1) * row_bytes) + dma_col;
+    const uint32_t m0 = ring0 + s * kMlaStageBytes + dma_first * 1024;
+    static_for<kDma>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value;
+      dma16<64 * (2 * DH + 4 * k)>(voff, dw.addr, m0 + 4096 * k);
+    });
   };
-  auto dma_all = [&](const Refill& r) __attribute__((always_inline)) {
-    static_for<kMlaDmaPerTile>([&](auto kc) __attribute__((always_inline)) { dma(r, kc); });
-  };
-  // Every tile step issues exactly one refill (9 DMAs per wave): once the
-  // worker's tiles run out, the last real refill is issued again (it rewrites
-  // a stage with the data it already holds), so every wait count below is a
-  // constant and no branch guards a DMA. The kernel drains them before exit.
-  Refill next_refill;  // the refill prepared during the current tile
-  Refill pending;      // the refill the next score phase issues
-
-  // Ring schedule: step t reads stage t % 4 (scores of tile t) and stage
-  // (t - 1) % 4 (values of tile t - 1), and its score phase issues the refill
-  // with tile t + 2 into stage (t + 2) % 4, whose last reader (the values of
-  // tile t - 2) finished before the barrier that ended step t - 1. So two
-  // stages are read and two are in flight at any time.
-  //
-  // (Re)start the ring at tile t (unit u): load tiles t and t + 1, prepare the
-  // refill with tile t + 2 and wait until tile t has landed everywhere.
+  // (Re)start the ring at tile t (unit u): load tiles t .. t + ahead - 1 and
+  // wait until tile t has landed everywhere.
   auto restart = [&](int64_t t, int64_t u) __attribute__((always_inline)) {
-    dw = walker_at(t, u);
-    for (int j = 0; j < 2; ++j) {
-      if (t + j < wend) next_refill = prepare();  // uniform
-      dma_all(next_refill);
-    }
-    // past the worker's last tile the step re-issues the last real refill:
-    // same data into the same stage (it only makes later waits more
-    // conservative)
-    if (t + 2 < wend) next_refill = prepare();  // uniform
-    pending = next_refill;
-    wait_vmcnt<kMlaDmaPerTile>();
+    walker_at(static_cast<int>(t - wstart), u);
+    static_for<kMlaAhead>([&](auto jc) __attribute__((always_inline)) {
+      dma_tile(stage_of(t + decltype(jc)::value));
+    });
+    wait_vmcnt<(kMlaAhead - 1) * kDma>();
     block_sync();
-  };
-  // End of step t (every read of stages t, t - 1 and of the weights issued):
-  // prepare the refill with tile t + 3, which becomes pending (issued by step
-  // t + 1), and wait until tile t + 1 has landed. The refill issued by this
-  // step (tile t + 2) is the only one allowed to stay in flight. The walker
-  // runs here rather than among the value MFMAs: issued as one block there it
-  // starves the matrix core, and here its rare scalar loads (a unit change)
-  // find no LDS read in flight.
-  auto end_tile = [&](int64_t t) __attribute__((always_inline)) {
-    wait_lgkm0();
-    if (t + 3 < wend) next_refill = prepare();  // uniform
-    pending = next_refill;
-    wait_vmcnt<kMlaDmaPerTile>();
-    block_sync();
-  };
-  // DMA j of the pending refill, issued after k-step 4 j of a score phase (a
-  // burst of all nine at once lands as one block of LDS writes that stalls the
-  // score operand reads)
-  auto pending_dma = [&](auto ksc) __attribute__((always_inline)) {
-    constexpr int ks = decltype(ksc)::value;
-    if constexpr ((ks & 3) == 0 && ks / 4 < kMlaDmaPerTile) dma(pending, std::integral_constant<int, ks / 4>{});
   };
 
-  // ---- per-lane LDS operand offsets ------------------------------------------
-  // Lane l = 32 h + c32 (h = l / 32), and in 16-lane groups l = 16 G + 4 i + j.
-  // Score operand (A of v_mfma_f32_32x32x16_bf16) of k-step ks (dims 16 ks
-  // .. +15): token row c32, dims 16 ks + 8 h .. +7, i.e. 32-dim block ks / 2,
-  // token half c32 / 16, chunk 2 (ks % 2) + h of row c32 % 16:
-  //   koff[ks % 2] + 2048 (ks / 2)
-  int koff[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) koff[q] = ((lane >> 4) & 1) * 1024 + 16 * mla_slot(lane & 15, 2 * q + (lane >> 5));
-  // Value operand (A) of M-tile mt (dims 32 mt .. +31) and token step kk
-  // (tokens 16 kk .. +15), through two transpose reads rd = 0, 1: the lane
-  // addresses token 8 (G / 2) + 4 rd + i of half kk and dims 32 mt + 16 (G % 2)
-  // + 4 j .. +3, i.e. chunk 2 (G % 2) + j / 2, byte 8 (j % 2):
-  //   voff[rd] + 2048 mt + 1024 kk
-  // and receives dim 32 mt + l % 32, tokens 8 h + 4 rd .. +3 of the step.
+  // ---- per-lane LDS offsets -----------------------------------------------------------
+  // score operand (A of the 16x16x32 MFMA): token n16, dims 32 ks + 8 g4 .. +7
+  const int koff = 16 * mla_slot(n16, g4) + 1024 * 9 * DH;
+  // value operand (A of the 32x32x16 MFMA) of dim tile mt through two transposing
+  // reads rd: lane l addresses token 8 (g4 / 2) + 4 rd + n16 / 4, dims
+  // 16 (g4 % 2) + 4 (l % 4) .. +3 of the block, and receives dim 32 mt + l % 32,
+  // tokens 8 (l / 32) + 4 rd .. +3
   int voff[2];
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
-    const int G = lane >> 4, i = (lane & 15) >> 2, j = lane & 3;
-    voff[rd] = 16 * mla_slot(8 * (G >> 1) + 4 * rd + i, 2 * (G & 1) + (j >> 1)) + 8 * (j & 1);
+    const int T = 8 * (g4 >> 1) + 4 * rd + (n16 >> 2), cc = 2 * (g4 & 1) + ((lane & 3) >> 1);
+    voff[rd] = 16 * mla_slot(T, cc) + 8 * (lane & 1) + 1024 * kMlaDvTiles * wave;
   }
+  // weights this wavefront writes: head tile nt_mine = 2 hg + DH, heads 16 i + n16,
+  // tokens 4 g4 .. 4 g4 + 3 -> 8 bytes of the reader lane n16 + 16 i + 32 (g4 / 2)
+  const int nt_mine = 2 * hg + DH;
+  const int pw_off = 1024 * nt_mine + 16 * (n16 + 32 * (g4 >> 1)) + 8 * (g4 & 1);
 
-  restart(wstart, ld_uniform(ws.wunit + worker));
+  const int64_t w_unit0 = ld_uniform(ws.wunit + worker);
+  restart(wstart, w_unit0);
 
-  int64_t cur_u = ld_uniform(ws.wunit + worker);  // unit of the tile being computed
+  int64_t cur_u = w_unit0;  // unit of the tile being computed
   int64_t tile = wstart;
-  float m_hint = -INFINITY;  // reference for a replayed piece (this lane's head)
-  bool replay = false;       // the current piece is a replay (at most one per piece)
-  const int h = lane >> 5;   // token quarter-row group of the score layout, k-half of the operands
+  float m_hint[2] = {-INFINITY, -INFINITY};  // reference for a replayed piece (this lane's two heads)
+  bool replay = false;                       // the current piece is a replay (at most one per piece)
 
   while (tile < wend) {
     while (ld_uniform(ws.prefix + cur_u + 1) <= tile) ++cur_u;
@@ -452,225 +362,241 @@ mla_attn_kernel(AttnParams p, int workers) {
                                static_cast<int>(rb / p.batch));
     const int64_t piece_tile0 = tile, piece_end = tile + (lt_hi - lt_lo);
 
-    // Q operand (B of the score MFMA): head 32 wave + l % 32, dims 16 ks + 8 h
-    // .. +7, all 36 k-steps in VGPRs
-    bf16x8_t qop[kMlaKSteps];
+    // Q operand (B of the score MFMA) of k-step ks, head tile ht: head
+    // 64 hg + 16 ht + n16, dims 288 DH + 32 ks + 8 g4 .. +7
+    bf16x8_t qop[kMlaKSteps][4];
     {
       const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) +
-                           ((static_cast<int64_t>(b) * p.q_len + qi) * kMlaHeads + kMlaHeadsPerWave * wave +
-                            (lane & 31)) * kMlaDk + 8 * h;
+                           ((static_cast<int64_t>(b) * p.q_len + qi) * kMlaHeads + 64 * hg + n16) * kMlaDk +
+                           288 * DH + 8 * g4;
 #pragma unroll
-      for (int ks = 0; ks < kMlaKSteps; ++ks) qop[ks] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * ks);
-      if (!(c2_in > 0.f)) {  // uniform
+      for (int ks = 0; ks < kMlaKSteps; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < kMlaKSteps; ++ks) {
-          u32x4_t w = __builtin_bit_cast(u32x4_t, qop[ks]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = (w[j] & q_keep) ^ q_flip;
-          qop[ks] = __builtin_bit_cast(bf16x8_t, w);
-        }
-      }
+        for (int ht = 0; ht < 4; ++ht)
+          qop[ks][ht] = *reinterpret_cast<const bf16x8_t*>(qb + 16 * kMlaDk * ht + 32 * ks);
     }
     // Q is complete here, so no wait for it lands inside the tile loop (where
     // it would also drain the tiles in flight).
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- piece state ------------------------------------------------------------
-    // Weights are exp2(s c2 - m_ref) with m_ref fixed for the piece (the first
-    // tile's max unless a replay hands one in); mx tracks the largest exponent
-    // seen, for the replay vote and the next reference. O^T[dim, head] of
-    // M-tile mt, N-tile nt (o[4 mt + nt]): lane l holds head 32 nt + l % 32,
-    // dims 128 wave + 32 mt + 8 (r / 4) + 4 h + r % 4.
-    float m_ref = m_hint, mx = -INFINITY, lsum = 0.f, esum = 0.f;
+    // ---- piece state ------------------------------------------------------------------
+    // This lane's two heads (i = 0, 1): 64 hg + 32 DH + 16 i + n16. Weights are
+    // exp2(s c2 - m_ref[i]); mx[i] tracks the largest exponent for the replay vote.
+    float m_ref[2] = {m_hint[0], m_hint[1]};
+    float mx[2] = {-INFINITY, -INFINITY}, esum[2] = {0.f, 0.f}, lsum[2] = {0.f, 0.f};
+    bool need_ref = !replay;  // uniform
+    // O^T[dim, head] of M-tile mt, N-tile nt (o[4 mt + nt]): lane l holds head
+    // 32 nt + l % 32, dims 128 wave + 32 mt + 8 (r / 4) + 4 (l / 32) + r % 4
     f32x16_t o[kMlaDvTiles * kMlaHeadTiles];
 #pragma unroll
     for (int i = 0; i < kMlaDvTiles * kMlaHeadTiles; ++i) o[i] = f32x16_t{};
-    bool need_ref = !replay;  // uniform
 
-    // ---- score MFMAs of one tile: S^T[token, head], lane l holding head l % 32,
-    // tokens 8 (r / 4) + 4 h + r % 4 of register r; each k-step's MFMA depends
-    // on the one before it; the pending refill goes out between them --------------
-    auto scores = [&](const char* st, f32x16_t& s, auto&& tail) __attribute__((always_inline)) {
-      s = f32x16_t{};
-      bf16x8_t ka[kMlaKPf + 1];
-      auto kread = [&](int ks) __attribute__((always_inline)) {
-        ka[ks % (kMlaKPf + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff[ks & 1] + 2048 * (ks >> 1));
-      };
+    // ---- pipeline ------------------------------------------------------------------------------
+    f32x4_t s[4];   // partial scores: token 4 g4 + j, head 64 hg + 16 ht + n16
+    bf16x8_t kf[kMlaKAhead + 1];  // K operands, read kMlaKAhead k-steps (six MFMAs each) ahead
+    auto kread = [&](const char* st, int ks) __attribute__((always_inline)) {
+      kf[ks % (kMlaKAhead + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff + 1024 * ks);
+    };
+    // send the partner its heads' partial scores (head tiles 2 (1 - DH), +1)
+    auto send = [&](char* xb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < kMlaKPf; ++j) kread(j);
-      static_for<kMlaKSteps>([&](auto ksc) __attribute__((always_inline)) {
-        constexpr int ks = decltype(ksc)::value;
-        if constexpr (ks + kMlaKPf < kMlaKSteps) kread(ks + kMlaKPf);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kMlaKPf + 1)], qop[ks], s, 0, 0, 0);
-        pending_dma(ksc);
-        // the value phase's first operand reads go out once the K ring stops
-        // refilling, so that their latency hides behind the last score MFMAs
-        if constexpr (ks == kMlaKSteps - kMlaKPf) tail();
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<f32x4_t*>(xb + 2048 * wave + 1024 * i + 16 * lane) = s[2 * (1 - DH) + i];
+    };
+    f32x4_t rcv[2];
+    auto receive = [&](const char* xb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        rcv[i] = *reinterpret_cast<const f32x4_t*>(xb + 2048 * (wave ^ 1) + 1024 * i + 16 * lane);
     };
 
-    // ---- softmax of one tile: weight r (0 .. 15) of this lane; pw[d] packs
-    // weights 2 d, 2 d + 1 (tokens 8 (d / 2) + 4 h + 2 (d % 2) + {0, 1})
-    f32x16_t s_cur;
-    uint32_t pw[8];
-    float pe_lo = 0.f;
-    auto weight = [&](int r) __attribute__((always_inline)) {
-      if (r >= 16) return;
-      const float x = fmaf(s_cur[r], c2, -m_ref);
-      mx = fmaxf(mx, x);
-      const float pe = __builtin_amdgcn_exp2f(x);  // v_exp_f32; results below 2^-126 flush to 0
-      esum += pe;
-      if (r & 1) {
-        const bf16x2_t pk = pack_bf16(pe_lo, pe);
-        pw[r >> 1] = __builtin_bit_cast(uint32_t, pk);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{__bf16(1.f), __bf16(1.f)}, lsum, false);
-      } else {
-        pe_lo = pe;
+    // softmax of this lane's 8 scores of the tile being normalised (sf: head i,
+    // token 4 g4 + j), one element e = 4 i + j at a time in three parts so that
+    // the stream can spread them between MFMAs; on the last tile of the unit
+    // tokens >= len are masked after scaling (only a step without a next tile
+    // can hold it)
+    f32x4_t sf[2];
+    uint32_t pw[2][2];
+    float xe[8];
+    auto soft_a = [&](int e, int tok0, bool last, auto mask_c) __attribute__((always_inline)) {
+      const int i = e >> 2, j = e & 3;
+      xe[e] = fmaf(sf[i][j], c2, -m_ref[i]);
+      if constexpr (decltype(mask_c)::value) {
+        if (last && tok0 + 4 * g4 + j >= len) xe[e] = -INFINITY;
       }
+      mx[i] = fmaxf(mx[i], xe[e]);
     };
-
-    // ---- weights to LDS -------------------------------------------------------------
-    // B operand of token step kk: lane l needs head l % 32, tokens 16 kk + 8 h ..
-    // +7. A lane holds tokens 4 h + {0..3} + 8 q (q = 2 kk, 2 kk + 1): swapping the
-    // upper half of the q = 2 kk words with the lower half of the q = 2 kk + 1
-    // words (v_permlane32_swap) gives every lane its 8 tokens, in order, which
-    // go to block 2 wave + kk of the weight buffer (one contiguous 1 KB store).
-    auto store_weights = [&](char* pbuf) __attribute__((always_inline)) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4_t pb;
-#pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(pw[4 * kk + w2], pw[4 * kk + 2 + w2], false, false);
-          pb[w2] = sw[0];
-          pb[2 + w2] = sw[1];
-        }
-        *reinterpret_cast<u32x4_t*>(pbuf + 1024 * (2 * wave + kk) + 16 * lane) = pb;
-      }
+    auto soft_b = [&](int e) __attribute__((always_inline)) {
+      xe[e] = __builtin_amdgcn_exp2f(xe[e]);  // v_exp_f32; results below 2^-126 flush to 0
+      esum[e >> 2] += xe[e];
     };
-
-    // ---- value MFMAs of one tile: dims 128 wave .. +127, all heads -----------------
-    // step idx = 4 kk + mt (kk outer, so that the two MFMAs into one accumulator
-    // are 16 apart): the A operand V^T of dims 128 wave + 32 mt .. +31, tokens
-    // 16 kk .. +15 through two transpose reads, kept in a ring indexed by the
-    // step, feeds the four N-tiles; the B operands (weights) of token step kk,
-    // N-tile nt are pb[kk][nt]. vstart() issues the reads the first steps need
-    // (called from the end of a score phase); values() runs the MFMAs with
-    // `slice(j)` (VALU work: two softmax weights of the next tile) in their
-    // shadow.
-    bf16x8_t pb[2][kMlaHeadTiles];
-    s16x4_t vb[kMlaVPf + 1][2];
-    auto vread = [&](const char* st, int idx) __attribute__((always_inline)) {
-      const int mt = idx % kMlaDvTiles, kk = idx / kMlaDvTiles;
-      const char* a0 = st + 2048 * (kMlaDvTiles * wave + mt) + 1024 * kk;
-      vb[idx % (kMlaVPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0 + voff[0]));
-      vb[idx % (kMlaVPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(a0 + voff[1]));
+    auto soft_c = [&](int e) __attribute__((always_inline)) {  // e odd: pack elements e - 1, e
+      const int i = e >> 2, q = (e & 3) >> 1;
+      const bf16x2_t pk = bf16x2_t{static_cast<__bf16>(xe[e - 1]), static_cast<__bf16>(xe[e])};
+      pw[i][q] = __builtin_bit_cast(uint32_t, pk);
+      lsum[i] = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{__bf16(1.f), __bf16(1.f)}, lsum[i], false);
     };
-    auto bread = [&](const char* pbuf, int kk) __attribute__((always_inline)) {
+    auto set_ref = [&](int tok0, bool last) __attribute__((always_inline)) {
 #pragma unroll
-      for (int nt = 0; nt < kMlaHeadTiles; ++nt)
-        pb[kk][nt] = *reinterpret_cast<const bf16x8_t*>(pbuf + 1024 * (2 * nt + kk) + 16 * lane);
-    };
-    auto vstart = [&](const char* st, const char* pbuf) __attribute__((always_inline)) {
-      bread(pbuf, 0);
-#pragma unroll
-      for (int j = 0; j < kMlaVPf; ++j) vread(st, j);
-    };
-    auto values = [&](const char* st, const char* pbuf, auto&& slice) __attribute__((always_inline)) {
-#pragma unroll
-      for (int idx = 0; idx < kMlaValSteps; ++idx) {
-        if (idx + kMlaVPf < kMlaValSteps) vread(st, idx + kMlaVPf);
-        const int mt = idx % kMlaDvTiles, kk = idx / kMlaDvTiles;
-        const s16x4_t* v = vb[idx % (kMlaVPf + 1)];
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int nt = 0; nt < kMlaHeadTiles; ++nt)
-          o[kMlaHeadTiles * mt + nt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk][nt], o[kMlaHeadTiles * mt + nt], 0, 0, 0);
-        if (idx == 0) bread(pbuf, 1);
-        slice(idx);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
-    // Before the weights of tile t: mask tokens past the shard's end (last
-    // tile only) and, on a piece's first tile, set the reference max.
-    auto prep = [&](int64_t t) __attribute__((always_inline)) {
-      const int tok0 = static_cast<int>(t - ubeg) * kMlaTile;
-      if (tok0 + kMlaTile > len) {  // uniform
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (tok0 + 8 * (r >> 2) + 4 * h + (r & 3) >= len) s_cur[r] = -INFINITY;
-      }
-      if (need_ref) {  // uniform
+      for (int i = 0; i < 2; ++i) {
         float mt = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s_cur[r] * c2);
-        m_ref = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        need_ref = false;
+        for (int j = 0; j < 4; ++j)
+          if (!(last && tok0 + 4 * g4 + j >= len)) mt = fmaxf(mt, sf[i][j] * c2);
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        m_ref[i] = fmaxf(mt, __shfl_xor(mt, 32, 64));
       }
     };
-
-    // Step t: scores of tile t, then the values of tile t - 1 (weights in LDS
-    // buffer (t - 1) % 2) with the softmax of tile t in their shadow, then tile
-    // t's weights to buffer t % 2; the barrier that ends the step publishes
-    // them. The piece's first step has no values and the last tile's values
-    // follow the loop.
-    auto two_weights = [&](int j) __attribute__((always_inline)) {
-      weight(2 * j);
-      weight(2 * j + 1);
-    };
-    auto no_slice = [](int) __attribute__((always_inline)) {};
-    auto no_tail = []() __attribute__((always_inline)) {};
-    scores(lds + stage_of(tile) * kMlaStageBytes, s_cur, no_tail);
-    prep(tile);
+    auto store_weights = [&](char* pb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) weight(r);
-    store_weights(pbuf + kMlaPBytes * (tile & 1));
-    end_tile(tile);
-    for (int64_t t = tile + 1; t < piece_end; ++t) {
-      const char* vst = lds + stage_of(t - 1) * kMlaStageBytes;
-      const char* vpb = pbuf + kMlaPBytes * ((t - 1) & 1);
-      scores(lds + stage_of(t) * kMlaStageBytes, s_cur,
-             [&]() __attribute__((always_inline)) { vstart(vst, vpb); });
-      prep(t);
-      values(vst, vpb, two_weights);
-      store_weights(pbuf + kMlaPBytes * (t & 1));
-      end_tile(t);
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<u32x2_t*>(pb + pw_off + 256 * i) = u32x2_t{pw[i][0], pw[i][1]};
+    };
+
+    // value operands: weights of every head (B, pbv[nt]) and V^T of dim tile mt
+    // (A, through two transposing reads into va[mt % 2])
+    s16x4_t va[2][2];
+    bf16x8_t pbv[kMlaHeadTiles];
+    auto vread = [&](const char* st, int mt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+        va[mt & 1][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(st + voff[rd] + 1024 * mt));
+    };
+
+    // One MFMA stream over the 9 score k-steps: the score MFMAs of the next
+    // tile (kNext: four per k-step, one per head tile), the value MFMAs of the
+    // previous tile (kPrev: two per k-step, dim tile ks / 2 with head tiles
+    // 2 (ks % 2) and + 1) and the softmax of the current tile (kSoft: element ks
+    // of this lane's eight). With one wavefront per SIMD the instructions issue
+    // in order, so the stream is written MFMA by MFMA with a small group of
+    // other instructions (operand reads, softmax parts) after each, pinned by
+    // scheduling barriers: they issue while the MFMA before them runs.
+    // Interleaving the two products also keeps every score accumulator's next
+    // MFMA several MFMAs behind the last one.
+    auto stream = [&](auto next_c, auto prev_c, auto soft_c_, const char* stn, const char* stp, const char* pbp,
+                      int tok0, bool last) __attribute__((always_inline)) {
+      constexpr bool kNext = decltype(next_c)::value, kPrev = decltype(prev_c)::value;
+      constexpr bool kSoft = decltype(soft_c_)::value;
+      const std::bool_constant<!kNext> mask_c{};
+      if constexpr (kPrev) {
+#pragma unroll
+        for (int nt = 0; nt < kMlaHeadTiles; ++nt)
+          pbv[nt] = *reinterpret_cast<const bf16x8_t*>(pbp + 1024 * nt + 16 * lane);
+        vread(stp, 0);
+      }
+      if constexpr (kNext)
+#pragma unroll
+        for (int j = 0; j < kMlaKAhead; ++j) kread(stn, j);
+      auto score_mfma = [&](int ks, int ht) __attribute__((always_inline)) {
+        if (ks == 0)
+          mfma_score_first(s[ht], kf[0], qop[0][ht]);
+        else
+          mfma_score(s[ht], kf[ks % (kMlaKAhead + 1)], qop[ks][ht]);
+      };
+      static_for<kMlaKSteps>([&](auto ksc) __attribute__((always_inline)) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr bool kVal = kPrev && ks < 2 * kMlaDvTiles;
+        constexpr bool kSm = kSoft && ks < 8;
+        constexpr int mt = ks / 2, nt0 = 2 * (ks % 2);
+        bf16x8_t a;
+        if constexpr (kVal)
+          a = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_shufflevector(va[mt & 1][0], va[mt & 1][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (kNext) score_mfma(ks, 0);
+        if constexpr (kNext && ks + kMlaKAhead < kMlaKSteps) kread(stn, ks + kMlaKAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kVal) mfma_acc(o[kMlaHeadTiles * mt + nt0], a, pbv[nt0]);
+        if constexpr (kVal && ks % 2 == 0 && mt + 1 < kMlaDvTiles) vread(stp, mt + 1);
+        if constexpr (kSm) soft_a(ks, tok0, last, mask_c);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kNext) score_mfma(ks, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kNext) score_mfma(ks, 2);
+        if constexpr (kSm) soft_b(ks);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kVal) mfma_acc(o[kMlaHeadTiles * mt + nt0 + 1], a, pbv[nt0 + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kNext) score_mfma(ks, 3);
+        if constexpr (kSm && (ks & 1)) soft_c(ks);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (kNext) score_settle(s);
+    };
+
+    // Step t (after the barrier that ends step t - 1): the partner's partial of
+    // tile t, the DMA of tile t + ahead into the stage of tile t - 2, then one
+    // stream with the scores of tile t + 1 (if in the piece), the values of tile
+    // t - 1 (if in the piece) and the softmax of tile t; tile t's weights to
+    // buffer t % 2, tile t + 1's partial scores to the partner, and the barrier
+    // (after this wave's DMAs of tile t + 2 have landed).
+    auto step = [&](int64_t t, auto next_c, auto prev_c) __attribute__((always_inline)) {
+      constexpr bool kNext = decltype(next_c)::value;
+      receive(sh.xbuf + kMlaXBytes * (t & 1));
+      dma_tile(stage_of(t + kMlaAhead));
+      const int tok0 = static_cast<int>(t - ubeg) * kMlaTile;
+      const bool last = tok0 + kMlaTile > len;  // uniform
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sf[i] = s[2 * DH + i] + rcv[i];
+      if (need_ref) {  // uniform: the piece's first tile
+        set_ref(tok0, last);
+        need_ref = false;
+      }
+      stream(next_c, prev_c, std::true_type{}, sh.ring + stage_of(t + 1) * kMlaStageBytes,
+             sh.ring + stage_of(t - 1) * kMlaStageBytes, sh.pbuf + kMlaPBytes * ((t - 1) & 1), tok0, last);
+      store_weights(sh.pbuf + kMlaPBytes * (t & 1));
+      if constexpr (kNext) send(sh.xbuf + kMlaXBytes * ((t + 1) & 1));
+      // this wave's DMAs of tile t + 2 are done once at most those of the three
+      // later tiles are in flight
+      wait_vmcnt<(kMlaAhead - 2) * kDma>();
+      wait_lgkm0();
+      block_sync();
+    };
+
+    // prologue: the scores of the piece's first tile, sent to the partner
+    stream(std::true_type{}, std::false_type{}, std::false_type{}, sh.ring + stage_of(tile) * kMlaStageBytes, nullptr,
+           nullptr, 0, false);
+    send(sh.xbuf + kMlaXBytes * (tile & 1));
+    wait_vmcnt<(kMlaAhead - 2) * kDma>();  // tile + 1, which step `tile` reads
+    wait_lgkm0();
+    block_sync();
+    if (piece_end - tile == 1) {  // uniform
+      step(tile, std::false_type{}, std::false_type{});
+    } else {
+      step(tile, std::true_type{}, std::false_type{});
+      for (int64_t t = tile + 1; t < piece_end - 1; ++t) step(t, std::true_type{}, std::true_type{});
+      step(piece_end - 1, std::false_type{}, std::true_type{});
     }
-    {
-      const char* vst = lds + stage_of(piece_end - 1) * kMlaStageBytes;
-      const char* vpb = pbuf + kMlaPBytes * ((piece_end - 1) & 1);
-      vstart(vst, vpb);
-      values(vst, vpb, no_slice);
-    }
+    // the last tile's values
+    stream(std::false_type{}, std::true_type{}, std::false_type{}, nullptr,
+           sh.ring + stage_of(piece_end - 1) * kMlaStageBytes, sh.pbuf + kMlaPBytes * ((piece_end - 1) & 1), 0,
+           false);
     tile = piece_end;
 
-    // ---- replay vote (block-uniform) and normalisers ----------------------------
-    // This wave's heads: normaliser (sum of the rounded weights) and fp32 weight
-    // sum over both token halves of the lane pair (l, l ^ 32).
-    const float lt_ = lsum + __shfl_xor(lsum, 32, 64);
-    const float et = esum + __shfl_xor(esum, 32, 64);
-    const int my_head = kMlaHeadsPerWave * wave + (lane & 31);
-    // the replay votes of the waves and the normaliser of each head go to the
-    // weight buffer of tile piece_end: its last readers (the values of tile
-    // piece_end - 2) finished before the last step's barrier, and its next
-    // writer (the next piece's first step) comes after the barriers below
-    float* s_norm = reinterpret_cast<float*>(pbuf + kMlaPBytes * (piece_end & 1));
-    int* s_vote = reinterpret_cast<int*>(s_norm + kMlaHeads);
-    const int wave_bad = __any(mx > kMlaRefSlack) ? 1 : 0;  // every lane takes part in the wave vote
-    if (lane == 0) s_vote[wave] = wave_bad;
-    if (h == 0) s_norm[my_head] = lt_;
-    wait_lgkm0();  // votes and normalisers are in LDS before the barrier
+    // ---- replay vote (block-uniform) and normalisers ---------------------------------------
+    // Sums over the four lane groups holding the other tokens of each head.
+    float lt[2], et[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lt[i] = lsum[i] + __shfl_xor(lsum[i], 16, 64);
+      lt[i] += __shfl_xor(lt[i], 32, 64);
+      et[i] = esum[i] + __shfl_xor(esum[i], 16, 64);
+      et[i] += __shfl_xor(et[i], 32, 64);
+    }
+    const int wave_bad = __any(mx[0] > kMlaRefSlack || mx[1] > kMlaRefSlack) ? 1 : 0;
+    if (lane == 0) sh.s_vote[wave] = wave_bad;
+    if (lane < 16) {
+      sh.s_norm[32 * nt_mine + lane] = lt[0];
+      sh.s_norm[32 * nt_mine + 16 + lane] = lt[1];
+    }
+    wait_lgkm0();
     block_sync();
     int any_bad = 0;
 #pragma unroll
-    for (int w = 0; w < kMlaWaves; ++w) any_bad |= s_vote[w];
+    for (int w = 0; w < kMlaWaves; ++w) any_bad |= sh.s_vote[w];
     float inv[kMlaHeadTiles];  // 1 / normaliser of head 32 nt + l % 32
 #pragma unroll
-    for (int nt = 0; nt < kMlaHeadTiles; ++nt) inv[nt] = 1.f / s_norm[32 * nt + (lane & 31)];
+    for (int nt = 0; nt < kMlaHeadTiles; ++nt) inv[nt] = 1.f / sh.s_norm[32 * nt + (lane & 31)];
     wait_lgkm0();
     block_sync();  // every wave has read votes and normalisers before they are written again
     // One replay always suffices for finite scores (its reference is the
@@ -678,25 +604,28 @@ mla_attn_kernel(AttnParams p, int workers) {
     // non-finite inputs, which then simply propagate.
     if (any_bad && !replay) {
       replay = true;
-      // replay the piece with the largest scaled score seen as the reference
-      const float ms = mx + m_ref;
-      m_hint = fmaxf(ms, __shfl_xor(ms, 32, 64));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float ms = mx[i] + m_ref[i];
+        ms = fmaxf(ms, __shfl_xor(ms, 16, 64));
+        m_hint[i] = fmaxf(ms, __shfl_xor(ms, 32, 64));
+      }
       wait_vmcnt<0>();
       block_sync();
       tile = piece_tile0;
-      cur_u = ld_uniform(ws.wunit + worker);
+      cur_u = w_unit0;
       restart(piece_tile0, cur_u);
       continue;
     }
     replay = false;
-    m_hint = -INFINITY;
+    m_hint[0] = m_hint[1] = -INFINITY;
 
-    // ---- piece end --------------------------------------------------------------
+    // ---- piece end --------------------------------------------------------------------------
     // O rows: this wave's dims of every head; LSE / (m_ref, normaliser, weight
-    // sum): this wave's heads.
+    // sum): this wave's 32 heads (lanes 0..15, heads 16 i + lane of tile nt_mine).
     const bool whole = (lt_lo == 0) && (lt_hi == uend - ubeg);
     const int which = (lt_lo == 0) ? 1 : 0;  // 0: the unit began before this worker
-    const int dim0 = kMlaDvTiles * 32 * wave + 4 * h;
+    const int dim0 = kMlaDvTiles * 32 * wave + 4 * (lane >> 5);
     if (whole) {
       const int64_t row0 = cur_u * kMlaHeads;  // = ((r * batch + b) * q_len + i) * Hq
 #pragma unroll
@@ -711,7 +640,11 @@ mla_attn_kernel(AttnParams p, int workers) {
                 f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]} * inv[nt];
           }
       }
-      if (h == 0) p.out_lse[row0 + my_head] = (m_ref + __log2f(et)) * DCP_LN2;
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          p.out_lse[row0 + 32 * nt_mine + 16 * i + lane] = (m_ref[i] + __log2f(et[i])) * DCP_LN2;
+      }
     } else {
       float* part = ws.part + (static_cast<int64_t>(worker) * 2 + which) * kMlaHeads * (kMlaDv + kPartExtra);
 #pragma unroll
@@ -725,15 +658,41 @@ mla_attn_kernel(AttnParams p, int workers) {
             *reinterpret_cast<f32x4_t*>(dst + 32 * mt + 8 * q) = f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
           }
       }
-      if (h == 0) {
-        float* dst = part + my_head * (kMlaDv + kPartExtra);
-        dst[kMlaDv] = m_ref;
-        dst[kMlaDv + 1] = lt_;
-        dst[kMlaDv + 2] = et;
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float* dst = part + (32 * nt_mine + 16 * i + lane) * (kMlaDv + kPartExtra);
+          dst[kMlaDv] = m_ref[i];
+          dst[kMlaDv + 1] = lt[i];
+          dst[kMlaDv + 2] = et[i];
+        }
       }
     }
   }
   wait_vmcnt<0>();  // refills issued past the last tile still write this workgroup's LDS
+}
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(kMlaThreads, kMlaThreads), amdgpu_waves_per_eu(1, 1)))
+mla_attn_kernel(AttnParams p, int workers) {
+  __shared__ __attribute__((aligned(16))) char ring[kMlaStages * kMlaStageBytes];
+  __shared__ __attribute__((aligned(16))) char pbuf[2 * kMlaPBytes];
+  __shared__ __attribute__((aligned(16))) char xbuf[2 * kMlaXBytes];
+  __shared__ float s_norm[kMlaHeads];
+  __shared__ int s_vote[kMlaWaves];
+  const int worker = blockIdx.x;
+  const int64_t U = split_units(p);
+  SplitWs ws = split_ws(p.workspace, U, workers);
+  const int64_t T = ld_uniform(ws.prefix + U);
+  if (T == 0 || worker >= workers) return;
+  const int64_t tpw = (T + workers - 1) / workers;
+  const int64_t wstart = static_cast<int64_t>(worker) * tpw;
+  if (wstart >= T) return;
+  const int64_t wend = min(T, wstart + tpw);
+  const MlaShared sh{ring, pbuf, xbuf, s_norm, s_vote};
+  if ((threadIdx.x >> 6) & 1)
+    mla_worker<1>(p, sh, workers, ws, wstart, wend);
+  else
+    mla_worker<0>(p, sh, workers, ws, wstart, wend);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,13 +703,12 @@ bool mla_supported(const AttnParams& p) {
   if (p.q_dtype != DCP_BF16 || kv.dtype != DCP_BF16) return false;
   if (kv.v != nullptr || kv.num_kv_heads != 1 || p.num_q_heads != kMlaHeads) return false;
   if (kv.head_dim_k != kMlaDk || kv.head_dim_v != kMlaDv) return false;
-  if (kv.block_size % 16 != 0) return false;
+  if (kv.block_size % kMlaTile != 0) return false;
   if (kv.k_stride[4] != 1) return false;
   for (int i = 0; i < 4; ++i)
     if ((kv.k_stride[i] * 2) % 16 != 0) return false;
   if (reinterpret_cast<uintptr_t>(kv.k) % 16) return false;
-  // block byte stride in 32 bits, offsets within a block in 31
-  if (kv.k_stride[1] * 2 >= (int64_t(1) << 32)) return false;
+  // offsets within a block in 31 bits (a row offset is a 32-bit lane offset)
   if (static_cast<int64_t>(kv.block_size) * kv.k_stride[3] * 2 >= (int64_t(1) << 31)) return false;
   if (static_cast<int64_t>(p.rank_count) * p.batch * p.q_len >= (int64_t(1) << 31)) return false;
   if (p.tpu != 1) return false;  // one query token per unit
