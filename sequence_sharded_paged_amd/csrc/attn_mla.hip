@@ -155,6 +155,14 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
                : "memory", "m0");
 }
 
+// LDS offset of lane l's 16 bytes in a 4 KB buffer read or written with one
+// 128-bit access per lane: 16-lane quarter q of the wave at 1 KB q. On gfx950
+// a 128-bit LDS access whose four quarters share one 1 KB line costs three
+// bank-conflict cycles (measured with SQ_LDS_BANK_CONFLICT); quarters 1 KB
+// apart cost none. Buffers accessed this way interleave four 256-byte rows
+// (selected by the caller's offset) per 1 KB line.
+__device__ __forceinline__ int quad_off(int lane) { return 1024 * (lane >> 4) + 16 * (lane & 15); }
+
 // Slot (16-byte unit) of chunk c (0..3) of row t (0..15) inside a 1 KB block.
 __device__ __forceinline__ int mla_slot(int t, int c) { return 16 * c + (t ^ (4 * c)); }
 
@@ -338,10 +346,13 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     const int T = 8 * (g4 >> 1) + 4 * rd + (n16 >> 2), cc = 2 * (g4 & 1) + ((lane & 3) >> 1);
     voff[rd] = 16 * mla_slot(T, cc) + 8 * (lane & 1) + 1024 * kMlaDvTiles * wave;
   }
-  // weights this wavefront writes: head tile nt_mine = 2 hg + DH, heads 16 i + n16,
-  // tokens 4 g4 .. 4 g4 + 3 -> 8 bytes of the reader lane n16 + 16 i + 32 (g4 / 2)
+  // Weight buffer: the B operand of N-tile nt for lane l (head 32 nt + l % 32,
+  // tokens 8 (l / 32) .. +7) at 256 nt + quad_off(l). This wavefront writes
+  // N-tile nt_mine = 2 hg + DH, each lane its reader's 16 bytes (after a swap
+  // of 16-lane rows, see store_weights).
   const int nt_mine = 2 * hg + DH;
-  const int pw_off = 1024 * nt_mine + 16 * (n16 + 32 * (g4 >> 1)) + 8 * (g4 & 1);
+  const int quad = quad_off(lane);
+  const int pw_off = 256 * nt_mine + quad;
 
   const int64_t w_unit0 = ld_uniform(ws.wunit + worker);
   restart(wstart, w_unit0);
@@ -398,17 +409,18 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     auto kread = [&](const char* st, int ks) __attribute__((always_inline)) {
       kf[ks % (kMlaKAhead + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff + 1024 * ks);
     };
-    // send the partner its heads' partial scores (head tiles 2 (1 - DH), +1)
+    // send the partner its heads' partial scores (head tiles 2 (1 - DH), +1):
+    // wavefront w's part i at 4 KB (w / 2) + 256 (2 (w % 2) + i) + quad_off(l)
     auto send = [&](char* xb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<f32x4_t*>(xb + 2048 * wave + 1024 * i + 16 * lane) = s[2 * (1 - DH) + i];
+        *reinterpret_cast<f32x4_t*>(xb + 4096 * hg + 256 * (2 * DH + i) + quad) = s[2 * (1 - DH) + i];
     };
     f32x4_t rcv[2];
     auto receive = [&](const char* xb) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        rcv[i] = *reinterpret_cast<const f32x4_t*>(xb + 2048 * (wave ^ 1) + 1024 * i + 16 * lane);
+        rcv[i] = *reinterpret_cast<const f32x4_t*>(xb + 4096 * hg + 256 * (2 * (1 - DH) + i) + quad);
     };
 
     // softmax of this lane's 8 scores of the tile being normalised (sf: head i,
@@ -448,10 +460,20 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
         m_ref[i] = fmaxf(mt, __shfl_xor(mt, 32, 64));
       }
     };
+    // A lane holds tokens 4 g4 .. +3 of its two heads i (16 i + n16 of the
+    // N-tile); the reader lane wants 8 consecutive tokens of one head. Swapping
+    // 16-lane rows (odd rows of head 0's words with even rows of head 1's)
+    // leaves lane l with head (l / 16) % 2, tokens 8 (l / 32) .. +7: exactly
+    // reader lane l's operand, stored with one 128-bit write.
     auto store_weights = [&](char* pb) __attribute__((always_inline)) {
+      u32x4_t v;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<u32x2_t*>(pb + pw_off + 256 * i) = u32x2_t{pw[i][0], pw[i][1]};
+      for (int q = 0; q < 2; ++q) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(pw[0][q], pw[1][q], false, false);
+        v[q] = sw[0];
+        v[2 + q] = sw[1];
+      }
+      *reinterpret_cast<u32x4_t*>(pb + pw_off) = v;
     };
 
     // value operands: weights of every head (B, pbv[nt]) and V^T of dim tile mt
@@ -482,7 +504,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
       if constexpr (kPrev) {
 #pragma unroll
         for (int nt = 0; nt < kMlaHeadTiles; ++nt)
-          pbv[nt] = *reinterpret_cast<const bf16x8_t*>(pbp + 1024 * nt + 16 * lane);
+          pbv[nt] = *reinterpret_cast<const bf16x8_t*>(pbp + 256 * nt + quad);
         vread(stp, 0);
       }
       if constexpr (kNext)
