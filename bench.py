@@ -844,7 +844,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # untimed steps before the timed ones: the first ~25 ms of sustained load
+    # run at changing clocks (an MLA step settles from 2.9 ms to 1.8 ms over
+    # its first 12 steps), so the default warms up past that
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default=None,
                     help=f"one workload only (default: {DEFAULT_WORKLOAD} as the headline, plus the per-config block)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
