@@ -593,10 +593,13 @@ __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
     ck_d0[k] = (c - i * cpt) * 8;
   }
 
+  // Unconditional loads (a chunk past the tile's tokens reloads token 0's):
+  // with a branch around them the compiler cannot count the loads in flight
+  // and waits for all of them before the first use.
   auto load_head = [&](int h, Raw8<kSrcBf16> (&raw)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (ck_tok[k] >= 0) raw[k] = load8<kSrcBf16>(p.v_new, ((t0 + ck_tok[k]) * H + h) * dv + ds + ck_d0[k]);
+      raw[k] = load8<kSrcBf16>(p.v_new, ((t0 + max(ck_tok[k], 0)) * H + h) * dv + ds + ck_d0[k]);
   };
   // converted elements of the tokens in groups g0 .. g0 + kVtGroups - 1 into their cells
   auto to_lds = [&](int h, const Raw8<kSrcBf16> (&raw)[4], int g0) __attribute__((always_inline)) {
@@ -668,13 +671,17 @@ __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
   };
   // all heads of one owner pass, one round of up to kVtGroups groups at a
   // time (one round unless the slots are scattered); within a round the next
-  // head's rows load while this one is stored
-  // Two register buffers: head h + 1's rows are requested before head h is
-  // converted, so their latency hides behind the conversion and the stores.
+  // head's rows load while this one is stored.
+  // Two register buffers: head h + 1's rows are requested once head h is
+  // converted, so their latency hides behind the barrier and the stores.
+  // (Requested before the conversion they would be waited for at its start:
+  // with stores of the previous head in flight, loads and stores complete out
+  // of order with respect to each other, and the compiler then waits for the
+  // vector memory counter to reach zero before using any load.)
   auto head_step = [&](int h, int g0, const Raw8<kSrcBf16> (&cur)[4], Raw8<kSrcBf16> (&nxt)[4])
       __attribute__((always_inline)) {
-    if (h + 1 < H) load_head(h + 1, nxt);
     to_lds(h, cur, g0);
+    if (h + 1 < H) load_head(h + 1, nxt);
     __syncthreads();
     store_cells(h, g0);
     __syncthreads();
