@@ -496,20 +496,25 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     // scheduling barriers: they issue while the MFMA before them runs.
     // Interleaving the two products also keeps every score accumulator's next
     // MFMA several MFMAs behind the last one.
-    auto stream = [&](auto next_c, auto prev_c, auto soft_c_, const char* stn, const char* stp, const char* pbp,
-                      int tok0, bool last) __attribute__((always_inline)) {
-      constexpr bool kNext = decltype(next_c)::value, kPrev = decltype(prev_c)::value;
-      constexpr bool kSoft = decltype(soft_c_)::value;
-      const std::bool_constant<!kNext> mask_c{};
-      if constexpr (kPrev) {
+    // The stream's first operands, issued before the step's other LDS traffic
+    // (the K operand of the first score MFMA first: LDS reads return in order)
+    auto stream_pre = [&](auto next_c, auto prev_c, const char* stn, const char* stp, const char* pbp)
+        __attribute__((always_inline)) {
+      if constexpr (decltype(next_c)::value)
+#pragma unroll
+        for (int j = 0; j < kMlaKAhead; ++j) kread(stn, j);
+      if constexpr (decltype(prev_c)::value) {
 #pragma unroll
         for (int nt = 0; nt < kMlaHeadTiles; ++nt)
           pbv[nt] = *reinterpret_cast<const bf16x8_t*>(pbp + 256 * nt + quad);
         vread(stp, 0);
       }
-      if constexpr (kNext)
-#pragma unroll
-        for (int j = 0; j < kMlaKAhead; ++j) kread(stn, j);
+    };
+    auto stream = [&](auto next_c, auto prev_c, auto soft_c_, const char* stn, const char* stp, const char* pbp,
+                      int tok0, bool last) __attribute__((always_inline)) {
+      constexpr bool kNext = decltype(next_c)::value, kPrev = decltype(prev_c)::value;
+      constexpr bool kSoft = decltype(soft_c_)::value;
+      const std::bool_constant<!kNext> mask_c{};
       auto score_mfma = [&](int ks, int ht) __attribute__((always_inline)) {
         if (ks == 0)
           mfma_score_first(s[ht], kf[0], qop[0][ht]);
@@ -554,6 +559,10 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     // (after this wave's DMAs of tile t + 2 have landed).
     auto step = [&](int64_t t, auto next_c, auto prev_c) __attribute__((always_inline)) {
       constexpr bool kNext = decltype(next_c)::value;
+      const char* stn = sh.ring + stage_of(t + 1) * kMlaStageBytes;
+      const char* stp = sh.ring + stage_of(t - 1) * kMlaStageBytes;
+      const char* pbp = sh.pbuf + kMlaPBytes * ((t - 1) & 1);
+      stream_pre(next_c, prev_c, stn, stp, pbp);
       receive(sh.xbuf + kMlaXBytes * (t & 1));
       dma_tile(stage_of(t + kMlaAhead));
       const int tok0 = static_cast<int>(t - ubeg) * kMlaTile;
@@ -564,8 +573,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
         set_ref(tok0, last);
         need_ref = false;
       }
-      stream(next_c, prev_c, std::true_type{}, sh.ring + stage_of(t + 1) * kMlaStageBytes,
-             sh.ring + stage_of(t - 1) * kMlaStageBytes, sh.pbuf + kMlaPBytes * ((t - 1) & 1), tok0, last);
+      stream(next_c, prev_c, std::true_type{}, stn, stp, pbp, tok0, last);
       store_weights(sh.pbuf + kMlaPBytes * (t & 1));
       if constexpr (kNext) send(sh.xbuf + kMlaXBytes * ((t + 1) & 1));
       // this wave's DMAs of tile t + 2 are done once at most those of the three
@@ -576,6 +584,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     };
 
     // prologue: the scores of the piece's first tile, sent to the partner
+    stream_pre(std::true_type{}, std::false_type{}, sh.ring + stage_of(tile) * kMlaStageBytes, nullptr, nullptr);
     stream(std::true_type{}, std::false_type{}, std::false_type{}, sh.ring + stage_of(tile) * kMlaStageBytes, nullptr,
            nullptr, 0, false);
     send(sh.xbuf + kMlaXBytes * (tile & 1));
@@ -590,9 +599,12 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
       step(piece_end - 1, std::false_type{}, std::true_type{});
     }
     // the last tile's values
-    stream(std::false_type{}, std::true_type{}, std::false_type{}, nullptr,
-           sh.ring + stage_of(piece_end - 1) * kMlaStageBytes, sh.pbuf + kMlaPBytes * ((piece_end - 1) & 1), 0,
-           false);
+    {
+      const char* stp = sh.ring + stage_of(piece_end - 1) * kMlaStageBytes;
+      const char* pbp = sh.pbuf + kMlaPBytes * ((piece_end - 1) & 1);
+      stream_pre(std::false_type{}, std::true_type{}, nullptr, stp, pbp);
+      stream(std::false_type{}, std::true_type{}, std::false_type{}, nullptr, stp, pbp, 0, false);
+    }
     tile = piece_end;
 
     // ---- replay vote (block-uniform) and normalisers ---------------------------------------
