@@ -21,11 +21,12 @@
 // 256-thread workgroup (one wavefront per SIMD) per CU, tiles of 16 tokens.
 // Per workgroup and tile:
 //   * the tile (16 rows x 1152 B) sits in a 7-stage LDS ring, filled straight
-//     from HBM with global_load_lds_dwordx4, in score-operand order: 18
-//     blocks of 1 KB, block ks holding dims 32 ks .. 32 ks + 31 of every row,
-//     16-byte chunk c of row t at slot 16 c + (t ^ 4 c) (the XOR keeps the
-//     transposing value-operand reads free of bank conflicts). Tiles are
-//     loaded five ahead, so a tile has about three steps to arrive;
+//     from HBM with global_load_lds_dwordx4, in score-operand order: the 16
+//     rows' 16-byte chunk c (dims 8 c .. 8 c + 7) of the 32-dim k-step ks
+//     form a 256-byte run, placed so that neither the score-operand reads nor
+//     the transposing value-operand reads meet LDS bank conflicts (ring_run,
+//     ring_swz). Tiles are loaded five ahead, so a tile has about three steps
+//     to arrive;
 //   * scores: the wavefront pair (0, 1) handles heads 0..63, the pair (2, 3)
 //     heads 64..127; within a pair, wavefront dh takes key dims 288 dh ..
 //     288 dh + 287. Each wavefront holds Q for its 64 heads x 288 dims (144
@@ -163,8 +164,20 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
 // (selected by the caller's offset) per 1 KB line.
 __device__ __forceinline__ int quad_off(int lane) { return 1024 * (lane >> 4) + 16 * (lane & 15); }
 
-// Slot (16-byte unit) of chunk c (0..3) of row t (0..15) inside a 1 KB block.
-__device__ __forceinline__ int mla_slot(int t, int c) { return 16 * c + (t ^ (4 * c)); }
+// Ring tile layout. Run (ks, c) (chunk c = 0..3 of k-step ks = 0..17, 16 rows
+// x 16 bytes) starts at ring_run(ks, c); row t sits at 16 (t ^ ring_swz(c))
+// in it. The runs of a score-operand read (one k-step, chunk c in 16-lane
+// quarter c) pair quarters 0, 1 and 2, 3 across different 1 KB lines, and
+// the row permutations 0, 12, 4, 8 keep both that read and the transposing
+// value read (rows 4 i .. 4 i + 3 of chunks 2 j, 2 j + 1 per quarter) free of
+// bank conflicts on gfx950 (measured per pattern with SQ_LDS_BANK_CONFLICT;
+// the plain 16 c + (t ^ 4 c) order within one 1 KB block cost four cycles per
+// score read). The 1 KB line 2 (ks / 2) + (c % 2) holds chunks c % 2 and
+// c % 2 + 2 of k-steps ks & ~1 and ks | 1, which is what one DMA writes.
+__device__ __forceinline__ constexpr int ring_run(int ks, int c) {
+  return 1024 * (2 * (ks >> 1) + (c & 1)) + 256 * (2 * (ks & 1) + (c >> 1));
+}
+__device__ __forceinline__ constexpr int ring_swz(int c) { return (0x84C0 >> (4 * c)) & 15; }
 
 // O += A . B on a 32x32x16 bf16 MFMA, a compiler builtin: the compiler then
 // tracks the wait states of every other instruction that reads or moves O,
@@ -240,13 +253,17 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
   };
 
   // ---- DMA walker ------------------------------------------------------------------
-  // DMA blocks of this wavefront: 2 DH + hg + 4 k (k < kDma): wavefronts with
-  // DH = 0 load five of the 18 blocks, DH = 1 four.
+  // DMA lines of this wavefront: 2 DH + hg + 4 k (k < kDma): wavefronts with
+  // DH = 0 load five of the tile's 18 lines of 1 KB, DH = 1 four. Line
+  // L = 2 j + hg holds the runs of chunks hg, hg + 2 of k-steps 2 j, 2 j + 1;
+  // lane l = 16 s + u writes position u of the line's run s (k-step
+  // 2 j + s / 2, chunk hg + 2 (s % 2)), i.e. row u ^ ring_swz(chunk). The
+  // k-steps' 64-byte column offset 128 j = 64 (2 DH + 4 k) is the DMA's
+  // immediate offset.
   constexpr int kDma = DH == 0 ? 5 : 4;
   const int dma_first = 2 * DH + hg;
-  // lane l = 16 c + u fetches row u ^ 4 c, chunk c of each block (slot l)
-  const int dma_row = n16 ^ (4 * g4);
-  const uint32_t dma_col = static_cast<uint32_t>(16 * g4 + 64 * hg);
+  const int dma_row = n16 ^ ring_swz(hg + 2 * (g4 & 1));
+  const uint32_t dma_col = static_cast<uint32_t>(64 * (g4 >> 1) + 32 * (g4 & 1) + 16 * hg);
   auto rel_end = [&](int64_t e) __attribute__((always_inline)) {
     return static_cast<int>(min(e - wstart, static_cast<int64_t>(INT32_MAX)));
   };
@@ -334,17 +351,19 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
   };
 
   // ---- per-lane LDS offsets -----------------------------------------------------------
-  // score operand (A of the 16x16x32 MFMA): token n16, dims 32 ks + 8 g4 .. +7
-  const int koff = 16 * mla_slot(n16, g4) + 1024 * 9 * DH;
-  // value operand (A of the 32x32x16 MFMA) of dim tile mt through two transposing
-  // reads rd: lane l addresses token 8 (g4 / 2) + 4 rd + n16 / 4, dims
-  // 16 (g4 % 2) + 4 (l % 4) .. +3 of the block, and receives dim 32 mt + l % 32,
-  // tokens 8 (l / 32) + 4 rd .. +3
+  // score operand (A of the 16x16x32 MFMA): token n16, dims 32 ks + 8 g4 .. +7,
+  // at koff + ring_run(9 DH + ks, 0)
+  const int koff = ring_run(0, g4) + 16 * (n16 ^ ring_swz(g4));
+  // value operand (A of the 32x32x16 MFMA) of dim tile mt (k-step 4 w + mt)
+  // through two transposing reads rd: lane l addresses token 8 (g4 / 2) + 4 rd
+  // + n16 / 4, dims 16 (g4 % 2) + 4 (l % 4) .. +3 of the k-step, and receives
+  // dim 32 mt + l % 32, tokens 8 (l / 32) + 4 rd .. +3; at voff[rd] +
+  // ring_run(mt, 0) (ring_run(4 w + mt, c) = ring_run(4 w, c) + ring_run(mt, 0))
   int voff[2];
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
     const int T = 8 * (g4 >> 1) + 4 * rd + (n16 >> 2), cc = 2 * (g4 & 1) + ((lane & 3) >> 1);
-    voff[rd] = 16 * mla_slot(T, cc) + 8 * (lane & 1) + 1024 * kMlaDvTiles * wave;
+    voff[rd] = ring_run(kMlaDvTiles * wave, cc) + 16 * (T ^ ring_swz(cc)) + 8 * (lane & 1);
   }
   // Weight buffer: the B operand of N-tile nt for lane l (head 32 nt + l % 32,
   // tokens 8 (l / 32) .. +7) at 256 nt + quad_off(l). This wavefront writes
@@ -407,7 +426,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     f32x4_t s[4];   // partial scores: token 4 g4 + j, head 64 hg + 16 ht + n16
     bf16x8_t kf[kMlaKAhead + 1];  // K operands, read kMlaKAhead k-steps (six MFMAs each) ahead
     auto kread = [&](const char* st, int ks) __attribute__((always_inline)) {
-      kf[ks % (kMlaKAhead + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff + 1024 * ks);
+      kf[ks % (kMlaKAhead + 1)] = *reinterpret_cast<const bf16x8_t*>(st + koff + ring_run(9 * DH + ks, 0));
     };
     // send the partner its heads' partial scores (head tiles 2 (1 - DH), +1):
     // wavefront w's part i at 4 KB (w / 2) + 256 (2 (w % 2) + i) + quad_off(l)
@@ -483,7 +502,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     auto vread = [&](const char* st, int mt) __attribute__((always_inline)) {
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd)
-        va[mt & 1][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(st + voff[rd] + 1024 * mt));
+        va[mt & 1][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(st + voff[rd] + ring_run(mt, 0)));
     };
 
     // One MFMA stream over the 9 score k-steps: the score MFMAs of the next
