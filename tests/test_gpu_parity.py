@@ -150,6 +150,21 @@ def test_nonpositive_softmax_scale(device, name, scale):
         check_against_oracle(inp, inp.run(algo=algo))
 
 
+@pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_bimodal", "mla_bf16_longtail_sink"])
+@pytest.mark.parametrize("bs,interleave", [(16, 1), (16, 16), (32, 8), (48, 16), (128, 64), (256, 1)])
+def test_block_sizes(device, name, bs, interleave):
+    """The MFMA kernels at block sizes other than the workloads' (any multiple
+    of 16): tiles that span several blocks (16- and 32-token blocks), blocks
+    whose size is not a power of two (48), and large blocks, with needles at
+    block boundaries so that a misplaced block shows."""
+    import dataclasses
+    w = dataclasses.replace(get_workload(name), block_size=bs, interleave=interleave)
+    case = make_case(w, device=device, seq_lens=[1, 17, 300, 2049, 0, 777], needles=3, needle_logit=20.0)
+    inp = DeviceInputs(case, device)
+    for algo in (GEN, FAST):
+        check_against_oracle(inp, inp.run(algo=algo))
+
+
 @pytest.mark.parametrize("name", ["gqa_bf16_32k", "gqa_fp8_binned", "mla_bf16_longtail_sink"])
 def test_rank_subsets(device, name):
     """One GPU computing only its own rank(s), as a per-GPU deployment would."""
