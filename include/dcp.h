@@ -255,7 +255,8 @@ int dcp_partial_decode_attn(const void* q, int32_t q_dtype, int32_t batch, int32
  *
  * The workspace is a static device array of DCP_NOALLOC_SCRATCH_BYTES that
  * the library holds on every device it runs this call on, from the first
- * such call there until the process ends. The call allocates no device or
+ * such call there until the process ends (with HIP's default deferred code
+ * loading; with eager loading, on every device from the library's load). The call allocates no device or
  * pinned memory; it fails with DCP_ERR_SCRATCH when
  * dcp_partial_decode_attn_workspace_size for the same arguments exceeds
  * DCP_NOALLOC_SCRATCH_BYTES (nothing is launched then). The kernels write
