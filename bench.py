@@ -2,9 +2,9 @@
 """Benchmark: one DCP decode step on one MI355X.
 
 A step is the whole hot path over one batch already resident in HBM: every
-DCP rank's partial decode attention over its sequence shard (planner, MFMA
-attention kernel, split combine) followed by the log-sum-exp merge across the
-ranks. The batch is synthetic (seeded; lengths, geometry and value
+DCP rank's partial decode attention over its sequence shard (the MFMA
+attention kernel and the split combine, with a planner kernel first for MLA)
+followed by the log-sum-exp merge across the ranks. The batch is synthetic (seeded; lengths, geometry and value
 distributions of the named workload). Prints ONE JSON line:
 
 * ``value``   - algorithmic KV bytes of the batch / step time, in GB/s

@@ -494,8 +494,8 @@ int dcp_gather_context(const dcp_kv_cache_t* kv, int32_t dcp_size, int32_t inter
  * dcp_profile_enable(1) makes every following dcp_partial_decode_attn and
  * dcp_partial_verify_attn call made by this host thread record a pair of HIP
  * events on its stream, right
- * before and right after its main attention kernel (the planner and the split
- * combine are outside the pair). dcp_profile_collect waits for the recorded
+ * before and right after its main attention kernel (the MLA planner and the
+ * split combine are outside the pair). dcp_profile_collect waits for the recorded
  * events, returns the summed elapsed milliseconds and the number of calls
  * since the last collect (or enable), and starts a new count.
  * dcp_profile_enable(0) stops recording. The events are created by the

@@ -44,6 +44,7 @@ constexpr float kGqaRescaleLog2 = 8.f;  // largest weight kept without rescaling
 template <bool kFp8>
 struct GqaTile {
   static constexpr int TOK = kFp8 ? 64 : 32;  // tokens per tile
+  static constexpr int TOK_LOG2 = kFp8 ? 6 : 5;
   static constexpr int NT = TOK / 16;         // score row tiles (16 tokens each)
   static constexpr int RUN = TOK / 4;         // consecutive tokens per lane group
   static constexpr int KS = TOK / 32;         // value-product k-steps
@@ -260,14 +261,18 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
   const int worker = __builtin_amdgcn_readfirstlane(blockIdx.x * kGqaWavesPerBlock + (threadIdx.x >> 6));
   const int n = lane & 15, qd = lane >> 4;
   const int G = p.group, rows = p.tpu * G;
-  const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, workers);
-  const int64_t T = ws.prefix[U];
-  if (worker >= workers || T == 0) return;
-  const int64_t tpw = (T + workers - 1) / workers;
-  const int64_t wstart = worker * tpw;
-  if (wstart >= T) return;
-  const int64_t wend = min(T, wstart + tpw);
+  SplitWs ws = split_ws(p.workspace, workers, 0);
+  __shared__ int64_t plan_lds[64 * kGqaWavesPerBlock + 16];
+  const SplitStart st = split_locate<64 * kGqaWavesPerBlock>(p, C::TOK_LOG2, workers, worker, plan_lds);
+  if (worker >= workers) return;  // (the grid's last workgroup may have spare wavefronts)
+  const int64_t wstart = st.wstart, wend = st.wend;
+  // the unit of the piece being computed and its tile range
+  int64_t u = st.u, ubeg = st.ubeg, uend = st.uend;
+  if (lane == 0 && worker == 0) ws.total[0] = st.total;
+  if (wstart >= wend) {
+    if (lane == 0) split_record(ws, worker, wstart, wend, -1, 0, 0);
+    return;
+  }
 
   const int bs = p.kv.block_size;
   const int64_t ks0 = p.kv.k_stride[0], ks1 = p.kv.k_stride[1], ks2 = p.kv.k_stride[2], ks3 = p.kv.k_stride[3];
@@ -276,11 +281,13 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
   const char* kbase = static_cast<const char*>(p.kv.k);
   const char* vbase = static_cast<const char*>(p.kv.v);
 
-  int64_t u = ws.wunit[worker];
   int64_t tile = wstart;
   while (tile < wend) {
-    const int64_t ubeg = ws.prefix[u], uend = ws.prefix[u + 1];
-    if (uend <= tile) { ++u; continue; }
+    while (uend <= tile) {  // uniform: on to the next unit with tiles
+      ++u;
+      ubeg = uend;
+      uend = ubeg + unit_tiles(p, u, C::TOK_LOG2);
+    }
     const int64_t t_lo = tile - ubeg, t_hi = min(wend, uend) - ubeg;  // unit-local tile range
     const UnitRef x = unit_ref(p, u);
     const int h = x.h, b = x.b, r = x.r;
@@ -384,8 +391,8 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
       }
     }
     tile = ubeg + t_hi;
-    ++u;
   }
+  if (lane == 0) split_record(ws, worker, wstart, wend, u, ubeg, uend);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,14 +436,13 @@ static int gqa_workers() {
 // Sized for the workers this device runs (split pieces: two per worker).
 size_t gqa_workspace_bytes(const AttnParams& p) {
   const int workers = p.kv.dtype == DCP_FP8_E4M3 ? gqa_workers<true>() : gqa_workers<false>();
-  return split_ws_bytes(split_units_host(p), workers, p.tpu * p.group, kGqaDim);
+  return split_ws_bytes(workers, 0, p.tpu * p.group, kGqaDim);
 }
 
 hipError_t launch_gqa_attn(const AttnParams& p) {
   const bool fp8 = p.kv.dtype == DCP_FP8_E4M3;
   const int workers = fp8 ? gqa_workers<true>() : gqa_workers<false>();
   const int tok = fp8 ? GqaTile<true>::TOK : GqaTile<false>::TOK;
-  launch_split_plan(p, tok, workers);
   const dim3 grid((workers + kGqaWavesPerBlock - 1) / kGqaWavesPerBlock);
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   if (fp8)
@@ -444,7 +450,7 @@ hipError_t launch_gqa_attn(const AttnParams& p) {
   else
     hipLaunchKernelGGL(gqa_attn_kernel<false>, grid, dim3(64 * kGqaWavesPerBlock), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  launch_split_combine<kGqaDim>(p, workers);
+  launch_split_combine<kGqaDim>(p, tok, workers, 0);
   return hipGetLastError();
 }
 

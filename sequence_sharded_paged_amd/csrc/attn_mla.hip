@@ -734,7 +734,7 @@ mla_attn_kernel(AttnParams p, int workers) {
   __shared__ int s_vote[kMlaWaves];
   const int worker = blockIdx.x;
   const int64_t U = split_units(p);
-  SplitWs ws = split_ws(p.workspace, U, workers);
+  SplitWs ws = split_ws(p.workspace, workers, U);
   const int64_t T = ld_uniform(ws.prefix + U);
   if (T == 0 || worker >= workers) return;
   const int64_t tpw = (T + workers - 1) / workers;
@@ -772,7 +772,7 @@ bool mla_supported(const AttnParams& p) {
 static int mla_workers() { return min(kMlaMaxWorkers, device_cu_count()); }
 
 size_t mla_workspace_bytes(const AttnParams& p) {
-  return split_ws_bytes(split_units_host(p), mla_workers(), kMlaHeads, kMlaDv);
+  return split_ws_bytes(mla_workers(), split_units_host(p), kMlaHeads, kMlaDv);
 }
 
 hipError_t launch_mla_attn(const AttnParams& p) {
@@ -781,7 +781,7 @@ hipError_t launch_mla_attn(const AttnParams& p) {
   if (p.ev_begin) (void)hipEventRecord(p.ev_begin, p.stream);
   hipLaunchKernelGGL(mla_attn_kernel, dim3(workers), dim3(kMlaThreads), 0, p.stream, p, workers);
   if (p.ev_end) (void)hipEventRecord(p.ev_end, p.stream);
-  launch_split_combine<kMlaDv>(p, workers);
+  launch_split_combine<kMlaDv>(p, kMlaTile, workers, split_units_host(p));
   return hipGetLastError();
 }
 

@@ -193,14 +193,34 @@ def test_invariance_over_dcp_and_interleave(device, name):
         assert np.abs(o - outs[0]).max() <= 2e-2
 
 
-def test_all_empty_batch(device):
-    w = get_workload("gqa_fp8_binned")
+@pytest.mark.parametrize("name", ["gqa_fp8_binned", "gqa_bf16_32k", "mla_bf16_bimodal"])
+def test_all_empty_batch(device, name):
+    """No local token anywhere: no worker has a tile, and the combine writes
+    every row from its empty-group pass."""
+    w = get_workload(name)
     case = make_case(w, device=device, seq_lens=[0, 0, 0])
     inp = DeviceInputs(case, device)
     for algo in (GEN, FAST):
         po, pl, o, lse = inp.run(algo=algo)
         assert torch.all(po == 0) and torch.all(torch.isneginf(pl))
         assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("name", ["gqa_fp8_binned", "mla_bf16_bimodal"])
+def test_many_pairs_per_thread_chunk(device, name):
+    """2,100 requests x 8 ranks = 16,800 (rank, request) pairs: the attention
+    kernel's split search gives each of its 256 threads a chunk of 66 pairs
+    (nine rounds of batched length loads), and a wavefront rescans the chunk
+    holding its first tile in two rounds of 64. Short and zero lengths leave
+    many ranks empty, so the combine's empty-group pass writes many rows.
+    Every request is checked."""
+    w = get_workload(name)
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 200, size=2100)
+    lens[rng.random(2100) < 0.2] = 0
+    case = make_case(w, device=device, seq_lens=[int(x) for x in lens])
+    inp = DeviceInputs(case, device)
+    check_against_oracle(inp, inp.run(algo=FAST))
 
 
 def test_token_major_v_layout_uses_generic(device):

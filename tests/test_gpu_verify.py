@@ -97,11 +97,13 @@ def test_verify_matches_across_kernels(device):
     assert (a[1][fin] - b[1][fin]).abs().max().item() <= 1e-3
 
 
-def test_verify_many_pairs_per_planner_thread(device):
-    """More (rank, request) pairs than planner threads (200 requests x 8 ranks
-    > 1024) with two token groups per pair (q_len = 3 > 16 / group) and 8 KV
-    heads: every unit's tile prefix comes from the planner's pair walk. Short
-    ragged lengths keep the oracle cheap; every request is checked."""
+def test_verify_many_pairs_per_thread_chunk(device):
+    """More (rank, request) pairs than the attention kernel's threads (200
+    requests x 8 ranks > 256), so each thread of its split search sums a chunk
+    of several pairs, with two token groups per pair (q_len = 3 > 16 / group)
+    and 8 KV heads: a worker's first unit is found by KV head and token group
+    inside its pair. Short ragged lengths keep the oracle cheap; every request
+    is checked."""
     w = get_workload("gqa_fp8_binned")
     rng = np.random.default_rng(7)
     lens = [int(x) for x in rng.integers(3, 400, size=200)]
