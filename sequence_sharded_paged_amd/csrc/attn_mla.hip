@@ -56,8 +56,8 @@
 //     t + 5 and runs one MFMA stream that interleaves the score MFMAs of tile
 //     t + 1 with the value MFMAs of tile t - 1 (independent accumulators, so
 //     neither waits on its own accumulation chain), with the softmax of tile t
-//     in its shadow; it then stores tile t's weights and sends tile t + 1's
-//     partial scores.
+//     in its shadow, and tile t's weights stored under its last MFMAs; it
+//     then sends tile t + 1's partial scores.
 //
 // DMA sources come from a scalar walker over the worker's tiles (a few scalar
 // instructions per tile); block-table entries are read through a 64-entry
@@ -530,7 +530,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
       }
     };
     auto stream = [&](auto next_c, auto prev_c, auto soft_c_, const char* stn, const char* stp, const char* pbp,
-                      int tok0, bool last) __attribute__((always_inline)) {
+                      int tok0, bool last, char* pbw) __attribute__((always_inline)) {
       constexpr bool kNext = decltype(next_c)::value, kPrev = decltype(prev_c)::value;
       constexpr bool kSoft = decltype(soft_c_)::value;
       const std::bool_constant<!kNext> mask_c{};
@@ -565,6 +565,8 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kNext) score_mfma(ks, 3);
         if constexpr (kSm && (ks & 1)) soft_c(ks);
+        // the weights are final after the last softmax part: stored under the last score MFMAs
+        if constexpr (kSoft && ks == kMlaKSteps - 1) store_weights(pbw);
         __builtin_amdgcn_sched_barrier(0);
       });
       if constexpr (kNext) score_settle(s);
@@ -573,8 +575,8 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     // Step t (after the barrier that ends step t - 1): the partner's partial of
     // tile t, the DMA of tile t + ahead into the stage of tile t - 2, then one
     // stream with the scores of tile t + 1 (if in the piece), the values of tile
-    // t - 1 (if in the piece) and the softmax of tile t; tile t's weights to
-    // buffer t % 2, tile t + 1's partial scores to the partner, and the barrier
+    // t - 1 (if in the piece) and the softmax of tile t, tile t's weights to
+    // buffer t % 2 (in the stream), tile t + 1's partial scores to the partner, and the barrier
     // (after this wave's DMAs of tile t + 2 have landed).
     auto step = [&](int64_t t, auto next_c, auto prev_c) __attribute__((always_inline)) {
       constexpr bool kNext = decltype(next_c)::value;
@@ -592,8 +594,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
         set_ref(tok0, last);
         need_ref = false;
       }
-      stream(next_c, prev_c, std::true_type{}, stn, stp, pbp, tok0, last);
-      store_weights(sh.pbuf + kMlaPBytes * (t & 1));
+      stream(next_c, prev_c, std::true_type{}, stn, stp, pbp, tok0, last, sh.pbuf + kMlaPBytes * (t & 1));
       if constexpr (kNext) send(sh.xbuf + kMlaXBytes * ((t + 1) & 1));
       // this wave's DMAs of tile t + 2 are done once at most those of the three
       // later tiles are in flight
@@ -605,7 +606,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
     // prologue: the scores of the piece's first tile, sent to the partner
     stream_pre(std::true_type{}, std::false_type{}, sh.ring + stage_of(tile) * kMlaStageBytes, nullptr, nullptr);
     stream(std::true_type{}, std::false_type{}, std::false_type{}, sh.ring + stage_of(tile) * kMlaStageBytes, nullptr,
-           nullptr, 0, false);
+           nullptr, 0, false, nullptr);
     send(sh.xbuf + kMlaXBytes * (tile & 1));
     wait_vmcnt<(kMlaAhead - 2) * kDma>();  // tile + 1, which step `tile` reads
     wait_lgkm0();
@@ -622,7 +623,7 @@ __device__ __forceinline__ void mla_worker(const AttnParams& p, const MlaShared&
       const char* stp = sh.ring + stage_of(piece_end - 1) * kMlaStageBytes;
       const char* pbp = sh.pbuf + kMlaPBytes * ((piece_end - 1) & 1);
       stream_pre(std::false_type{}, std::true_type{}, nullptr, stp, pbp);
-      stream(std::false_type{}, std::true_type{}, std::false_type{}, nullptr, stp, pbp, 0, false);
+      stream(std::false_type{}, std::true_type{}, std::false_type{}, nullptr, stp, pbp, 0, false, nullptr);
     }
     tile = piece_end;
 
