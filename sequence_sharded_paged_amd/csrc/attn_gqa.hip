@@ -340,8 +340,7 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
     // first tile would also wait for the second): rows past the shard's end
     // read the tile's first chunk instead and are masked afterwards. An odd
     // tile count leaves the piece's last tile to a step of its own after the
-    // loop (re-reading it as the second of a pair instead cost 3% of the fp8
-    // kernel's time).
+    // loop rather than loading it twice as the two tiles of a pair.
     // (tile indices inside one unit fit in 32 bits: a shard holds < 2^31 tokens)
     const int tb = static_cast<int>(t_lo), te = static_cast<int>(t_hi), t_last = te - 1;
     GqaIds ids_a = gqa_load_ids<kFp8>(bt, tb, len, bs, n, qd);
