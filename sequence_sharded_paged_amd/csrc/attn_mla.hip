@@ -74,7 +74,6 @@ constexpr int kMlaHeads = 128;
 constexpr int kMlaTile = 16;                                   // tokens per tile
 constexpr int kMlaStages = 7;                                  // LDS ring depth
 constexpr int kMlaAhead = 5;                                   // tiles loaded ahead of the scores
-constexpr int kMlaRowBytes = kMlaDk * 2;                       // 1152
 constexpr int kMlaBlocks = kMlaDk / 32;                        // 18 operand blocks of 1 KB per tile
 constexpr int kMlaStageBytes = kMlaBlocks * 1024;              // 18432
 constexpr int kMlaWaves = 4;
