@@ -268,7 +268,10 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
   const int64_t wstart = st.wstart, wend = st.wend;
   // the unit of the piece being computed and its tile range
   int64_t u = st.u, ubeg = st.ubeg, uend = st.uend;
-  if (lane == 0 && worker == 0) ws.total[0] = st.total;
+  if (lane == 0 && worker == 0) {
+    ws.total[0] = st.total;
+    ws.total[1] = workers;  // one record per worker
+  }
   if (wstart >= wend) {
     if (lane == 0) split_record(ws, worker, wstart, wend, -1, 0, 0);
     return;

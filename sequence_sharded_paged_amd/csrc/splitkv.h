@@ -33,16 +33,17 @@ constexpr int kCombineThreads = 256;
 // normaliser of O), the sum of the fp32 weights (the LSE) and one unused
 // float, so rows of a Dv divisible by 4 start on 16-byte boundaries.
 constexpr int kPartExtra = 4;
-// Per worker: the unit that starts inside the worker's tile range and runs
-// past its end (the one unit whose pieces the combine merges for it), as
-// {unit or -1, first tile, end tile, unused}.
+// Cut record: a unit cut between workers, as {unit or -1 (none), first tile,
+// end tile, worker holding its first tile}. Either one per worker (the unit
+// that starts inside the worker's range and runs past its end), or, from the
+// planner, one per cut unit and no more.
 constexpr int kCutRec = 4;
 
 struct SplitWs {
   int64_t* prefix;  // planned split: [U + 1] tile prefix over units, prefix[U] = total (else unused)
   int32_t* wunit;   // planned split: [workers] unit holding each worker's first tile (else unused)
-  int64_t* total;   // [1] tiles of all units
-  int64_t* cut;     // [workers][kCutRec], rewritten on every call
+  int64_t* total;   // [2]: tiles of all units, cut records to read
+  int64_t* cut;     // [up to workers][kCutRec], rewritten on every call
   float* part;      // [workers][2][rows][Dv + kPartExtra], rows = tpu * group
 };
 
@@ -57,8 +58,8 @@ __host__ __device__ inline SplitWs split_ws(void* base, int max_workers, int64_t
   w.wunit = reinterpret_cast<int32_t*>(p);
   p += align_up(static_cast<size_t>(max_workers) * sizeof(int32_t), 256);
   w.total = reinterpret_cast<int64_t*>(p);
-  w.cut = w.total + 1;
-  p += align_up(static_cast<size_t>(1 + max_workers * kCutRec) * sizeof(int64_t), 256);
+  w.cut = w.total + 2;
+  p += align_up(static_cast<size_t>(2 + max_workers * kCutRec) * sizeof(int64_t), 256);
   w.part = reinterpret_cast<float*>(p);
   return w;
 }
@@ -66,7 +67,7 @@ __host__ __device__ inline SplitWs split_ws(void* base, int max_workers, int64_t
 static inline size_t split_ws_bytes(int max_workers, int64_t plan_units, int rows, int dv) {
   size_t b = align_up(static_cast<size_t>(plan_units + 1) * sizeof(int64_t), 256);
   b += align_up(static_cast<size_t>(max_workers) * sizeof(int32_t), 256);
-  b += align_up(static_cast<size_t>(1 + max_workers * kCutRec) * sizeof(int64_t), 256);
+  b += align_up(static_cast<size_t>(2 + max_workers * kCutRec) * sizeof(int64_t), 256);
   b += static_cast<size_t>(max_workers) * 2 * rows * (dv + kPartExtra) * sizeof(float);
   return b;
 }
@@ -293,7 +294,7 @@ __device__ SplitStart split_locate(const AttnParams& p, int tok_log2, int worker
 // A worker's record for the combine (tile range [wstart, wend)): the unit of
 // its last piece when that unit starts inside the range and runs past its
 // end, else none (last_u = -1 for a worker without tiles). Written by one
-// lane; worker 0 also stores the total tiles in ws.total.
+// lane; worker 0 also stores the header (total tiles, one record per worker).
 __device__ __forceinline__ void split_record(const SplitWs& ws, int worker, int64_t wstart, int64_t wend,
                                              int64_t last_u, int64_t last_beg, int64_t last_end) {
   const bool cut = last_u >= 0 && last_beg >= wstart && last_end > wend;
@@ -301,7 +302,7 @@ __device__ __forceinline__ void split_record(const SplitWs& ws, int worker, int6
   rec[0] = cut ? last_u : -1;
   rec[1] = last_beg;
   rec[2] = last_end;
-  rec[3] = 0;
+  rec[3] = worker;
 }
 
 // Planned split (one block): tile prefix over units, the first unit of every
@@ -315,6 +316,7 @@ constexpr int kPlanThreads = 1024;
 static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnParams p, int tok_log2, int workers) {
   __shared__ int64_t wsum[kPlanThreads / 64];
   __shared__ int64_t total_s;
+  __shared__ int ncut_s;
   const int64_t U = split_units(p);
   SplitWs ws = split_ws(p.workspace, workers, U);
   const int H = p.kv.num_kv_heads, ntg = p.ntg;
@@ -323,7 +325,7 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
   const int chunk = (RB + kPlanThreads - 1) / kPlanThreads;
   const int rb0 = min(RB, tid * chunk), rb1 = min(RB, rb0 + chunk);
   const int b0 = p.batch > 0 ? rb0 % p.batch : 0, r0 = p.batch > 0 ? rb0 / p.batch : 0;
-  for (int w = tid; w < workers; w += kPlanThreads) ws.cut[static_cast<int64_t>(w) * kCutRec] = -1;
+  if (tid == 0) ncut_s = 0;
   int64_t s = 0;
   for (int rb = rb0, b = b0, r = r0; rb < rb1; ++rb) {
     int64_t srb = 0;
@@ -334,7 +336,7 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
   // block exclusive scan: within each wavefront, then over the 16 wavefront sums
   const int64_t incl = wave_incl_scan(s, lane);
   if (lane == 63) wsum[wid] = incl;
-  __syncthreads();  // (also orders the "none" records before the cut ones)
+  __syncthreads();
   int64_t before = 0;
   for (int w = 0; w < wid; ++w) before += wsum[w];
   if (tid == kPlanThreads - 1) total_s = before + incl;
@@ -360,12 +362,12 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
           ws.wunit[wfirst] = static_cast<int32_t>(u);
           cut |= wfirst * tpw > run;
         }
-        if (cut) {  // recorded by the worker holding the unit's first tile
-          int64_t* rec = ws.cut + floor_div_fp64(run, tpw) * kCutRec;
+        if (cut) {  // one record per cut unit, in no particular order (at most one per worker)
+          int64_t* rec = ws.cut + static_cast<int64_t>(atomicAdd(&ncut_s, 1)) * kCutRec;
           rec[0] = u;
           rec[1] = run;
           rec[2] = nxt;
-          rec[3] = 0;
+          rec[3] = floor_div_fp64(run, tpw);  // the worker holding its first tile
         }
         run = nxt;
       }
@@ -376,10 +378,12 @@ static __global__ void __launch_bounds__(kPlanThreads) split_plan_kernel(AttnPar
     ws.prefix[U] = T;
     ws.total[0] = T;
   }
+  __syncthreads();
+  if (tid == 0) ws.total[1] = ncut_s;
 }
 
-// Fixed grid; one wavefront per item. Items of the first kind are (worker,
-// row of a unit) for every worker's cut record, a row being (query token,
+// Fixed grid; one wavefront per item. Items of the first kind are (cut
+// record, row of its unit) for every record the workspace header lists, a row being (query token,
 // query head of the group): merge the pieces of the unit, or write O = 0 /
 // LSE = -inf for a row that sees no token of the unit (a query earlier than
 // every local token; its pieces carry m = -inf). Pieces are read four at a
@@ -403,7 +407,7 @@ __global__ void __launch_bounds__(kCombineThreads)
   SplitWs ws = split_ws(p.workspace, workers, plan_units);
   const int64_t T = ws.total[0];
   const int64_t tpw = T > 0 ? ceil_div_fp64(T, workers) : 1;
-  const int64_t items_cut = static_cast<int64_t>(workers) * rows;
+  const int64_t items_cut = ws.total[1] * rows;
   const int groups = p.rank_count * p.batch * p.ntg;  // < 2^31
   const int slots = p.tpu * p.num_q_heads;            // output rows of a token group
   const int64_t items = items_cut + static_cast<int64_t>((groups + 63) / 64) * slots;
@@ -435,11 +439,11 @@ __global__ void __launch_bounds__(kCombineThreads)
       }
       continue;
     }
-    const int wk = static_cast<int>(it / rows), c = static_cast<int>(it % rows);
-    const int64_t* rec = ws.cut + static_cast<int64_t>(wk) * kCutRec;
+    const int c = static_cast<int>(it % rows);
+    const int64_t* rec = ws.cut + (it / rows) * kCutRec;
     const int64_t u = rec[0];
     if (u < 0) continue;  // no unit starts in this worker's range and runs past it
-    const int64_t ubeg = rec[1], uend = rec[2];
+    const int64_t ubeg = rec[1], uend = rec[2], wk = rec[3];
     const UnitRef x = unit_ref(p, u);
     const int i = x.i0 + c / G;
     if (i >= x.i1) continue;  // a row past the request's last query token
