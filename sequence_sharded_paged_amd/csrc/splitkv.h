@@ -17,7 +17,7 @@
 //   * for the MLA kernel, whose register budget has no room for that walk, a
 //     one-block planner kernel first writes the tile prefix over units and
 //     every worker's first unit to the workspace (split_plan_kernel).
-// Either way every worker's cut record (below) and the total reach the
+// Either way the cut records (below), their count and the total reach the
 // workspace for the combine.
 #pragma once
 
