@@ -343,7 +343,9 @@ __global__ void __launch_bounds__(64 * kGqaWavesPerBlock)
     // first tile would also wait for the second): rows past the shard's end
     // read the tile's first chunk instead and are masked afterwards. An odd
     // tile count leaves the piece's last tile to a step of its own after the
-    // loop rather than loading it twice as the two tiles of a pair.
+    // loop rather than loading it twice as the two tiles of a pair (1.0% of
+    // the fp8 kernel's time and 1.8% of the bf16 one's, timed in one process
+    // on one pool against the loop that re-read it).
     // (tile indices inside one unit fit in 32 bits: a shard holds < 2^31 tokens)
     const int tb = static_cast<int>(t_lo), te = static_cast<int>(t_hi), t_last = te - 1;
     GqaIds ids_a = gqa_load_ids<kFp8>(bt, tb, len, bs, n, qd);
