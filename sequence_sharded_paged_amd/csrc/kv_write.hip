@@ -528,9 +528,7 @@ __global__ void __launch_bounds__(256) kv_vt_kernel(KvWriteParams p) {
 // leaves LDS with one 16-byte read and reaches the pool with one 16-byte store
 // (consecutive words of a block row by consecutive lanes). Up to kVtGroups
 // groups are staged at a time; tiles with more (scattered slots) take several
-// rounds per head. The cell of group g in dim row d is g ^ ((d / 8) % 8): the
-// sixteen lanes that convert one token's row write rows eight apart, and the
-// swizzle spreads them over the banks.
+// rounds per head (cells placed by vt16_cell).
 constexpr int kVtGroups = 8;  // 16-byte word groups staged in LDS at a time
 
 template <int kW>
@@ -555,10 +553,112 @@ __device__ __forceinline__ int vt16_group_pass(const KvWriteParams& p, int lane,
   return o.nvalid;
 }
 
+// The 16-byte cell of group g in dim row d of a tile's LDS cell buffer
+// ([dim][group], kVtGroups groups per row): g ^ ((d / 8) % 8), so that the
+// sixteen lanes converting one token's row (rows eight apart) spread over the
+// banks.
+__device__ __forceinline__ int vt16_cell(int d, int g) { return d * kVtGroups + (g ^ ((d >> 3) & 7)); }
+
+// A thread's four 8-element chunks of a tile's V rows (nd dims of ntok
+// tokens, nd / 8 chunks per token, 256 threads): chunk c = 256 k + thread is
+// token c / (nd / 8), dims 8 (c % (nd / 8)) .. +7; ck_tok[k] = -1 past the
+// tile's tokens.
+__device__ __forceinline__ void vt16_chunks(int nd, int ntok, int (&ck_tok)[4], int (&ck_d0)[4]) {
+  const int cpt = nd / 8, total = ntok * cpt;  // <= 1024
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = k * 256 + static_cast<int>(threadIdx.x);
+    const int i = c / cpt;
+    ck_tok[k] = c < total ? i : -1;
+    ck_d0[k] = (c - i * cpt) * 8;
+  }
+}
+
+// The tile's V^T words through LDS, step 1: this thread's chunks (token
+// ck_tok[k] or -1, dims ck_d0[k] .. +7) of one head, converted, into the cells
+// of their tokens' groups when the group is one of g0 .. g0 + kVtGroups - 1.
+template <int kDst, bool kSrcBf16>
+__device__ __forceinline__ void vt16_to_lds(const Raw8<kSrcBf16> (&raw)[4], const int (&ck_tok)[4],
+                                            const int (&ck_d0)[4], const int* s_col, int g0, double rcp,
+                                            uint4* s_cell) {
+  using St = typename Stored<kDst>::T;
+  constexpr int kW = 16 / static_cast<int>(sizeof(St));
+  char* cells = reinterpret_cast<char*>(s_cell);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = ck_tok[k], d0 = ck_d0[k];
+    if (i < 0) continue;
+    const int col = s_col[i];
+    const int gb = (col >= 0 ? col / kW : -1) - g0;
+    if (col < 0 || gb < 0 || gb >= kVtGroups) continue;
+    uint32_t q[8];
+    convert8<kDst, kSrcBf16>(raw[k], rcp, q);
+    const int u = col - (col / kW) * kW;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<St*>(cells + vt16_cell(d0 + e, gb) * 16 + u * sizeof(St)) = static_cast<St>(q[e]);
+  }
+}
+
+// Step 2: thread = (group gb of the round, dim), the round's groups rounded
+// up to a power of two; each cell goes to its pool word (head offset
+// head_off, dims ds .. ds + nd - 1). A word whose slots are all written is one
+// 16-byte store; a partial word (the ends of a run of slots) is stored in the
+// widest aligned pieces it fills: 8 bytes, 4 bytes, then single elements.
+template <int kDst>
+__device__ __forceinline__ void vt16_store_cells(const KvWriteParams& p, int64_t head_off, int ds, int nd, int g0,
+                                                 int groups, const uint32_t* s_gmask, const int64_t* s_gbase,
+                                                 const uint4* s_cell) {
+  using St = typename Stored<kDst>::T;
+  constexpr int kW = 16 / static_cast<int>(sizeof(St));
+  const int tid = threadIdx.x;
+  const int ng = min(groups - g0, kVtGroups);
+  int gp = 1;
+  while (gp < ng) gp *= 2;
+  const int gb = tid & (gp - 1);
+  if (gb >= ng) return;
+  const int g = g0 + gb;
+  const uint32_t mask = s_gmask[g];
+  const bool full = mask == (kW == 32 ? ~0u : (1u << kW) - 1);
+  const int64_t base = s_gbase[g] + head_off;
+  St* vpool = static_cast<St*>(p.kv.v);
+  const int64_t vdim = p.kv.v_stride[4];
+  for (int d = tid / gp; d < nd; d += 256 / gp) {
+    const uint4 v = s_cell[vt16_cell(d, gb)];
+    St* dst = vpool + base + static_cast<int64_t>(ds + d) * vdim;
+    if (full) {
+      *reinterpret_cast<uint4*>(dst) = v;
+      continue;
+    }
+    const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+    const St* el = reinterpret_cast<const St*>(&v);
+    constexpr int kHalf = kW / 2, kQuad = 4 / static_cast<int>(sizeof(St));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t hm = (mask >> (hh * kHalf)) & ((1u << kHalf) - 1);
+      if (hm == (1u << kHalf) - 1) {
+        *reinterpret_cast<uint2*>(dst + hh * kHalf) = uint2{dw[2 * hh], dw[2 * hh + 1]};
+        continue;
+      }
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int u0 = hh * kHalf + qq * kQuad;
+        const uint32_t qm = (mask >> u0) & ((1u << kQuad) - 1);
+        if (qm == (1u << kQuad) - 1) {
+          *reinterpret_cast<uint32_t*>(dst + u0) = dw[2 * hh + qq];
+        } else if (qm) {
+#pragma unroll
+          for (int u = u0; u < u0 + kQuad; ++u)
+            if ((mask >> u) & 1u) dst[u] = el[u];
+        }
+      }
+    }
+  }
+}
+
 template <int kDst, bool kSrcBf16>
 __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
-  using St = typename Stored<kDst>::T;
-  constexpr int kW = 16 / static_cast<int>(sizeof(St));  // slots per 16-byte word
+  constexpr int kW = 16 / static_cast<int>(sizeof(typename Stored<kDst>::T));  // slots per 16-byte word
   __shared__ uint64_t s_owners[kVtTokens];    // owners not yet written, per token
   __shared__ uint64_t s_first[kVtTokens];     // (first owner << kSlotBits) | its slot; all ones: none
   __shared__ uint32_t s_gmask[kVtTokens];     // slots of group g's word that a token of the pass writes
@@ -578,20 +678,10 @@ __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
   const int H = p.kv.num_kv_heads, dv = p.kv.head_dim_v;
   const int ds = blockIdx.y * kVtDims;
   const int nd = dv - ds < kVtDims ? dv - ds : kVtDims;
-  const int cpt = nd / 8, total = ntok * cpt;  // <= 1024
   const int64_t cap = static_cast<int64_t>(p.kv.num_blocks) * p.kv.block_size;
-  St* vpool = static_cast<St*>(p.kv.v);
-  const int64_t vdim = p.kv.v_stride[4], vhead = p.kv.v_stride[2];
-  char* cells = reinterpret_cast<char*>(s_cell);
-  // this thread's chunks (token, first dim), fixed for the whole tile (-1: none)
+  const int64_t vhead = p.kv.v_stride[2];
   int ck_tok[4], ck_d0[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = k * 256 + tid;
-    const int i = c / cpt;
-    ck_tok[k] = c < total ? i : -1;
-    ck_d0[k] = (c - i * cpt) * 8;
-  }
+  vt16_chunks(nd, ntok, ck_tok, ck_d0);
 
   // Unconditional loads (a chunk past the tile's tokens reloads token 0's):
   // with a branch around them the compiler cannot count the loads in flight
@@ -601,73 +691,13 @@ __global__ void __launch_bounds__(256) kv_vt16_kernel(KvWriteParams p) {
     for (int k = 0; k < 4; ++k)
       raw[k] = load8<kSrcBf16>(p.v_new, ((t0 + max(ck_tok[k], 0)) * H + h) * dv + ds + ck_d0[k]);
   };
-  // converted elements of the tokens in groups g0 .. g0 + kVtGroups - 1 into their cells
   auto to_lds = [&](int h, const Raw8<kSrcBf16> (&raw)[4], int g0) __attribute__((always_inline)) {
     double rcp = 1.0;
     if constexpr (kDst == DCP_FP8_E4M3) rcp = scale_rcp(p.kv.v_scale, h);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = ck_tok[k], d0 = ck_d0[k];
-      if (i < 0) continue;
-      const int col = s_col[i];
-      const int gb = (col >= 0 ? col / kW : -1) - g0;
-      if (col < 0 || gb < 0 || gb >= kVtGroups) continue;
-      uint32_t q[8];
-      convert8<kDst, kSrcBf16>(raw[k], rcp, q);
-      const int u = col - (col / kW) * kW;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = d0 + e;
-        *reinterpret_cast<St*>(cells + (d * kVtGroups + (gb ^ ((d >> 3) & 7))) * 16 + u * sizeof(St)) =
-            static_cast<St>(q[e]);
-      }
-    }
+    vt16_to_lds<kDst, kSrcBf16>(raw, ck_tok, ck_d0, s_col, g0, rcp, s_cell);
   };
-  // thread = (group gb, dim), the groups of the round rounded up to a power of two
   auto store_cells = [&](int h, int g0) __attribute__((always_inline)) {
-    const int ng = min(s_groups - g0, kVtGroups);
-    int gp = 1;
-    while (gp < ng) gp *= 2;
-    const int gb = tid & (gp - 1);
-    if (gb >= ng) return;
-    const int g = g0 + gb;
-    const uint32_t mask = s_gmask[g];
-    const bool full = mask == (kW == 32 ? ~0u : (1u << kW) - 1);
-    const int64_t base = s_gbase[g] + h * vhead;
-    for (int d = tid / gp; d < nd; d += 256 / gp) {
-      const uint4 v = s_cell[d * kVtGroups + (gb ^ ((d >> 3) & 7))];
-      St* dst = vpool + base + static_cast<int64_t>(ds + d) * vdim;
-      if (full) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
-        // the written slots in the widest aligned pieces they fill: 8 bytes,
-        // 4 bytes, then single elements (a run of slots leaves at most a
-        // ragged piece at each end)
-        const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
-        const St* el = reinterpret_cast<const St*>(&v);
-        constexpr int kHalf = kW / 2, kQuad = 4 / static_cast<int>(sizeof(St));
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const uint32_t hm = (mask >> (hh * kHalf)) & ((1u << kHalf) - 1);
-          if (hm == (1u << kHalf) - 1) {
-            *reinterpret_cast<uint2*>(dst + hh * kHalf) = uint2{dw[2 * hh], dw[2 * hh + 1]};
-            continue;
-          }
-#pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
-            const int u0 = hh * kHalf + qq * kQuad;
-            const uint32_t qm = (mask >> u0) & ((1u << kQuad) - 1);
-            if (qm == (1u << kQuad) - 1) {
-              *reinterpret_cast<uint32_t*>(dst + u0) = dw[2 * hh + qq];
-            } else if (qm) {
-#pragma unroll
-              for (int u = u0; u < u0 + kQuad; ++u)
-                if ((mask >> u) & 1u) dst[u] = el[u];
-            }
-          }
-        }
-      }
-    }
+    vt16_store_cells<kDst>(p, h * vhead, ds, nd, g0, s_groups, s_gmask, s_gbase, s_cell);
   };
   // all heads of one owner pass, one round of up to kVtGroups groups at a
   // time (one round unless the slots are scattered); within a round the next

@@ -133,10 +133,13 @@ def _slots_for(rng, T, R, N, bs, I):
 
 # Batches under 1024 tokens take the per-(token, head) kernel. Larger ones take
 # the one-token-per-wavefront row kernel when a token's row is 48..64 pieces
-# of 16 elements in aligned pools (the last two cases: 8 x 128 with a block
-# size that is not a power of two, 3 x 256 with 16 idle lanes; padded pools
-# fall back), else the general row kernel; V stored dim-major takes the
-# 64-token tile kernels (whose last tile is ragged in the cases below).
+# of 16 elements in aligned pools (8 x 128 with a block size that is not a
+# power of two, 3 x 256 with 16 idle lanes, 8 x 128 over 8 ranks; padded pools
+# fall back), else the general row kernel (4 x 128 is 32 pieces); V stored
+# dim-major takes the 64-token tile kernels (whose
+# last tile is ragged in every case below; the last two have 8 ranks, 16-byte
+# words of fp8 slots aligned in the pool, and scattered positions that give
+# tiles several rounds of word groups).
 GQA_CASES = [
     # (H, Dk, Dv, bs, R, I, N, T)
     (2, 16, 16, 16, 4, 1, 6, 70),
@@ -147,6 +150,8 @@ GQA_CASES = [
     (3, 24, 136, 8, 3, 8, 150, 1030),
     (8, 128, 128, 24, 4, 8, 40, 1301),
     (3, 256, 256, 16, 3, 16, 60, 1030),
+    (4, 128, 128, 64, 8, 64, 40, 1100),
+    (8, 128, 128, 32, 8, 1, 60, 1090),
 ]
 
 
