@@ -209,9 +209,9 @@ def test_segment_validation(L):
     p = _fake(64)
     f = L.dcp_partial_segment_attn
 
-    def call(seg_rank=1, rb=0, rc=2, part=p, ws_bytes=1 << 40, batch=4):
-        return f(p, native.DCP_BF16, batch, 8, ctypes.byref(_kv()), p, 4, 4, p, ctypes.c_float(0.1), 0, seg_rank,
-                 rb, rc, part, p, p, ctypes.c_size_t(ws_bytes), NULL)
+    def call(seg_rank=1, rb=0, rc=2, part=p, ws_bytes=1 << 40, batch=4, scale=0.1, stride=4, lens=p, algo=0):
+        return f(p, native.DCP_BF16, batch, 8, ctypes.byref(_kv()), p, stride, 4, lens, ctypes.c_float(scale), algo,
+                 seg_rank, rb, rc, part, p, p, ctypes.c_size_t(ws_bytes), NULL)
 
     assert call(seg_rank=-1) == INV
     assert call(rc=0) == INV
@@ -219,6 +219,11 @@ def test_segment_validation(L):
     assert call(part=NULL) == INV
     assert call(ws_bytes=16) == WS
     assert call(batch=0) == 0
+    # the segment's attention checks the arguments dcp_partial_decode_attn checks
+    for algo in (0, 1, 2):
+        assert call(scale=float("nan"), algo=algo) == INV
+        assert call(stride=3, algo=algo) == INV       # stride < seg_max_vblocks
+        assert call(lens=NULL, algo=algo) == INV
 
 
 def test_gather_validation(L):

@@ -17,20 +17,23 @@ from tests.harness import DeviceInputs, SegmentInputs, check_segment_against_ora
 
 pytestmark = pytest.mark.gpu
 
-GEN, FAST = dcp.DCP_ALGO_GENERIC, dcp.DCP_ALGO_FAST
+GEN, FAST, AUTO = dcp.DCP_ALGO_GENERIC, dcp.DCP_ALGO_FAST, dcp.DCP_ALGO_AUTO
 
+# Windows from one token to several hundred (300, 400, 600: a segment pool of
+# many blocks, units cut between workers in the MFMA path).
 CASES = {
     # name: (lengths, windows)
     "gqa_fp32_tiny": ([8, 37, 100], [1, 40]),
-    "gqa_bf16_32k": ([1, 17, 100, 257, 1000, 0], [1, 128]),
-    "gqa_fp8_binned": ([1, 64, 65, 513, 3000, 0], [64, 128]),
-    "mla_bf16_bimodal": ([1, 33, 65, 700, 2000], [32, 128]),
+    "gqa_bf16_32k": ([1, 17, 100, 257, 1000, 0], [1, 128, 300]),
+    "gqa_fp8_binned": ([1, 64, 65, 513, 3000, 0], [64, 128, 400]),
+    "mla_bf16_bimodal": ([1, 33, 65, 700, 2000], [32, 128, 600]),
     "mla_bf16_longtail_sink": ([5, 37, 600, 2049], [128]),
 }
 
 
 def _algos(name):
-    return [GEN] if name == "gqa_fp32_tiny" else [GEN, FAST]
+    # fp32 KV has no MFMA kernel: FAST refuses it, AUTO takes the generic kernel
+    return [GEN, AUTO] if name == "gqa_fp32_tiny" else [GEN, FAST]
 
 
 def _run(inp, sgi, seg_rank, algo):
