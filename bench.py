@@ -10,7 +10,9 @@ distributions of the named workload). Prints ONE JSON line:
 * ``value``   - algorithmic KV bytes of the batch / step time, in GB/s
                 (KV bytes = sum of context lengths x KV bytes per token);
 * ``roofline``- the main attention kernel alone, timed with HIP events that
-                the library records around it on the launch stream, against
+                the library records around it on the launch stream (in a
+                second loop of as many steps, so that the step time carries
+                no instrumentation), against
                 the 8 TB/s HBM peak; ``traffic`` comes from the committed
                 rocprofv3 counter summary when it was taken on the current
                 kernel source, else null;
@@ -98,6 +100,31 @@ def load_traffic(family, workload):
     if rec.get("source_sha256_16") != source_hash(family):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def timed_steps(step, steps):
+    """(ms per step, ms per main attention kernel): the steps are timed first
+    with nothing recorded between their launches, then as many again with the
+    library's HIP events around each attention kernel (events recorded on the
+    stream add a gap to every step, which would otherwise count as step time)."""
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    dcp.native.dcp_profile_enable(True)
+    dcp.native.dcp_profile_collect()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern_ms, launches = dcp.native.dcp_profile_collect()
+    dcp.native.dcp_profile_enable(False)
+    return ms, kern_ms / max(launches, 1)
 
 
 def blas_threads():
@@ -355,19 +382,7 @@ def bench_verify(args, vw):
     for _ in range(args.warmup):
         run.step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dcp.native.dcp_profile_enable(True)
-    dcp.native.dcp_profile_collect()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        run.step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern_ms, launches = dcp.native.dcp_profile_collect()
-    dcp.native.dcp_profile_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    kern_avg_ms = kern_ms / max(launches, 1)
+    ms, kern_avg_ms = timed_steps(run.step, args.steps)
     kv_bytes = case.kv_bytes()
     family = kernel_family(w)
     out = {
@@ -444,19 +459,8 @@ def bench_segment(args, sw):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    ms, kern_avg_ms = timed_steps(step, args.steps)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dcp.native.dcp_profile_enable(True)
-    dcp.native.dcp_profile_collect()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern_ms, launches = dcp.native.dcp_profile_collect()
-    dcp.native.dcp_profile_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    kern_avg_ms = kern_ms / max(launches, 1)
     # the segment call alone (its attention over the segments and the fold)
     start.record()
     for _ in range(args.steps):
@@ -705,19 +709,7 @@ def measure_decode(w, steps, warmup, cpu_budget_s):
     for _ in range(warmup):
         inp.step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dcp.native.dcp_profile_enable(True)
-    dcp.native.dcp_profile_collect()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        inp.step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern_ms, launches = dcp.native.dcp_profile_collect()
-    dcp.native.dcp_profile_enable(False)
-    ms = start.elapsed_time(stop) / steps
-    kern_avg_ms = kern_ms / max(launches, 1)
+    ms, kern_avg_ms = timed_steps(inp.step, steps)
     tokens = int(case.seq_lens.astype(np.int64).sum())
     kv_bytes = case.kv_bytes()
     family = kernel_family(w)
