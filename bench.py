@@ -414,15 +414,8 @@ def bench_verify(args, vw):
             "verified_tokens_per_s": round(case.batch * vw.q_len / (ms * 1e-3), 1),
             "kernel": KERNEL_NAMES[family],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(kv_bytes / (kern_avg_ms * 1e-3) / 1e9, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(kv_bytes / (kern_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(family, vw.name),
-            "kernel_avg_ms": round(kern_avg_ms, 5),
-        },
+        "roofline": attn_roofline(kv_bytes, verify_flops(w, case.seq_lens, vw.q_len), kern_avg_ms,
+                                  load_traffic(family, vw.name)),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -499,16 +492,9 @@ def bench_segment(args, sw):
             "segment_call_ms": round(seg_ms, 5),
             "kernel": KERNEL_NAMES[family],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(case.kv_bytes() / (kern_avg_ms * 1e-3) / 1e9, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(case.kv_bytes() / (kern_avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel_avg_ms": round(kern_avg_ms, 5),
-            "note": "the sharded attention kernel (the segment call is timed separately in config)",
-        },
+        "roofline": dict(attn_roofline(case.kv_bytes(), step_flops(w, int(case.seq_lens.astype(np.int64).sum())),
+                                       kern_avg_ms, None),
+                         note="the sharded attention kernel (the segment call is timed separately in config)"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -672,6 +658,38 @@ def step_flops(w, tokens):
     """Algorithmic matrix flops of one decode step: QK^T and PV over every
     cached token, for every query head."""
     return 2 * tokens * w.num_q_heads * (w.head_dim_k + w.head_dim_v)
+
+
+def attn_roofline(kv_bytes, flops, kern_avg_ms, traffic):
+    """Roofline of an attention kernel launch against the bound its arithmetic
+    intensity selects: the bf16 matrix peak when its flops per KV byte exceed
+    the ridge (2.5 PFLOP/s / 8 TB/s = 312.5, e.g. MLA with several query
+    tokens), else HBM. Both fractions are reported either way."""
+    s = kern_avg_ms * 1e-3
+    hbm = kv_bytes / s / 1e9
+    tf = flops / s / 1e12
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = flops / max(kv_bytes, 1) > ridge
+    r = {"bound": "mfma" if mfma_bound else "hbm",
+         "achieved": round(tf if mfma_bound else hbm, 2),
+         "peak": BF16_MFMA_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+         "unit": "TFLOP/s" if mfma_bound else "GB/s",
+         "frac": round((tf / BF16_MFMA_PEAK_TFLOPS) if mfma_bound else (hbm / HBM_PEAK_GBS), 4),
+         "traffic": traffic,
+         "kernel_avg_ms": round(kern_avg_ms, 5),
+         "flop_per_kv_byte": round(flops / max(kv_bytes, 1), 1),
+         "hbm_gbs": round(hbm, 2), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
+         "mfma_tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+    return r
+
+
+def verify_flops(w, seq_lens, q_len):
+    """Algorithmic matrix flops of one multi-token step: query token i of a
+    request of length L sees L - q_len + i + 1 positions."""
+    import numpy as np
+    L = np.asarray(seq_lens, dtype=np.int64)
+    seen = int((q_len * L - q_len * (q_len - 1) // 2).sum())
+    return 2 * seen * w.num_q_heads * (w.head_dim_k + w.head_dim_v)
 
 
 def step_bytes(w, case, out_elem):
