@@ -21,6 +21,9 @@ distributions of the named workload). Prints ONE JSON line:
 * ``per_config``- (default run) the same measurements for the GQA bf16, the
                 two MLA and the GQA fp8 decode workloads, each with a shorter
                 oracle sample, the MLA ones also against the bf16 MFMA peak;
+* ``hbm_read_ceiling`` - (default run) the device's measured streaming-read
+                rate (dcp_hbm_read_probe over 8 GiB); every decode roofline
+                then also carries ``frac_of_read_ceiling``;
 * ``layout``  - local lengths and the slot mapping (one decode step's new
                 tokens, and the bulk fill of every cached token) timed apart
                 from the step, with the oracle's brute-force mapper beside it.
@@ -775,6 +778,41 @@ def measure_decode(w, steps, warmup, cpu_budget_s):
     return res
 
 
+def measure_read_ceiling(nbytes=8 << 30, reps=10):
+    """The device's sustained streaming-read rate: dcp_hbm_read_probe over an
+    `nbytes` buffer (far past the 256 MB last-level cache), 3 untimed reads,
+    then `reps` timed with events. Taken first in the run, on a fresh
+    allocation: a buffer allocated where freed pools were reads up to ≈5%
+    slower."""
+    import torch
+    import sequence_sharded_paged_amd as dcp
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")  # (written once, as the KV pools are)
+    digest = torch.empty(dcp.dcp_hbm_read_probe_blocks(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        dcp.dcp_hbm_read_probe(buf, digest)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dcp.dcp_hbm_read_probe(buf, digest)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del buf, digest
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"gbs": round(gbs, 2), "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "bytes": nbytes,
+            "ms_per_read": round(ms, 4), "reads": reps, "kernel": "hbm_read_probe_kernel"}
+
+
+def with_ceiling(roofline, ceiling_gbs):
+    """The kernel's HBM rate also as a fraction of the measured read ceiling."""
+    hbm = roofline.get("hbm_gbs", roofline["achieved"] if roofline.get("unit") == "GB/s" else None)
+    if hbm is not None and ceiling_gbs:
+        roofline["frac_of_read_ceiling"] = round(hbm / ceiling_gbs, 4)
+    return roofline
+
+
 def measure_layout(w, steps, cpu_budget_s):
     """The layout steps of the path on one workload's batch, timed apart from
     the decode step: local lengths and the slot mapping of one decode step's
@@ -910,6 +948,8 @@ def main():
         return
     w = get_workload(name)
     cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget_s
+    full_run = args.workload is None and not args.no_per_config
+    ceiling = measure_read_ceiling() if full_run else None
     head = measure_decode(w, args.steps, args.warmup, cpu)
     cores, blas = host_cores()
     out = {
@@ -954,7 +994,7 @@ def main():
         cb["host_cores"] = cores
         cb["blas_threads"] = blas
         out["cpu_baseline"] = cb
-    if args.workload is None and not args.no_per_config:
+    if full_run:
         pc_cpu = 0.0 if args.no_cpu_baseline else args.per_config_cpu_budget_s
         per = {}
         for pname in PER_CONFIG:
@@ -972,6 +1012,13 @@ def main():
                   f"({r['pct_hbm_peak']:.1f}%), kernel frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
         out["per_config"] = per
         out["layout"] = measure_layout(w, 50, pc_cpu)
+        out["hbm_read_ceiling"] = ceiling
+        with_ceiling(out["roofline"], ceiling["gbs"])
+        for r in per.values():
+            with_ceiling(r["roofline"], ceiling["gbs"])
+        print(f"[bench] streaming-read ceiling {ceiling['gbs']:.0f} GB/s ({ceiling['pct_hbm_peak']:.1f}% of the "
+              f"8 TB/s peak); {w.name} kernel at {out['roofline'].get('frac_of_read_ceiling', 0) * 100:.1f}% of it",
+              file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

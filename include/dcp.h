@@ -505,6 +505,27 @@ int dcp_gather_context(const dcp_kv_cache_t* kv, int32_t dcp_size, int32_t inter
 int dcp_profile_enable(int on);
 int dcp_profile_collect(double* total_ms, int32_t* launches);
 
+/*
+ * Measurement hook: the device's sustained streaming-read rate, the measured
+ * ceiling that the decode kernels' HBM fractions are reported against next to
+ * the 8 TB/s specification (time a call with events on `stream`; rate =
+ * bytes / time).
+ *
+ * dcp_hbm_read_probe reads each of the `bytes` bytes of `buf` exactly once
+ * (16-byte non-temporal loads, each wavefront one contiguous run, a fixed grid
+ * of dcp_hbm_read_probe_blocks() workgroups) and writes digest[g] = the XOR of
+ * the 32-bit words that workgroup g read; the XOR of all digests is the XOR
+ * of every 32-bit word of the buffer.
+ *   buf     device, 16-byte aligned; bytes >= 0 and a multiple of 16
+ *   digest  device, uint32[digest_len], digest_len >= dcp_hbm_read_probe_blocks()
+ * dcp_hbm_read_probe_blocks() returns the workgroup count for the current
+ * device (4 per CU), or a negative status.
+ * Errors: DCP_ERR_INVALID_ARG (NULL or misaligned buffer, bad sizes),
+ * DCP_ERR_HIP. bytes == 0 launches nothing.
+ */
+int dcp_hbm_read_probe_blocks(void);
+int dcp_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* digest, int32_t digest_len, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

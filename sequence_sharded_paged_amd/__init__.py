@@ -14,6 +14,6 @@ from .native import (  # noqa: F401
     DCP_NOALLOC_SCRATCH_BYTES,
     dcp_partial_decode_attn_workspace_size, dcp_partial_segment_attn, dcp_partial_segment_attn_workspace_size,
     dcp_partial_verify_attn, dcp_partial_verify_attn_workspace_size,
-    dcp_slot_mapping, dcp_status_string,
+    dcp_slot_mapping, dcp_status_string, dcp_hbm_read_probe, dcp_hbm_read_probe_blocks,
 )
 from .cache import PagedKVCache  # noqa: F401

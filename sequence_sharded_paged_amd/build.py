@@ -18,7 +18,7 @@ LIBDIR = os.path.join(HERE, "lib")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(LIBDIR, "libdcp.so")
 
-SOURCES = ["abi.cpp", "layout.hip", "merge.hip", "attn_generic.hip", "attn_gqa.hip", "attn_mla.hip", "kv_write.hip", "gather.hip"]
+SOURCES = ["abi.cpp", "layout.hip", "merge.hip", "attn_generic.hip", "attn_gqa.hip", "attn_mla.hip", "kv_write.hip", "gather.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

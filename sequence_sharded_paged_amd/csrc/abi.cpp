@@ -388,6 +388,23 @@ int dcp_partial_verify_attn(const void* q, int32_t q_dtype, int32_t batch, int32
                       workspace_bytes, stream);
 }
 
+int dcp_hbm_read_probe_blocks(void) {
+  const int b = hbm_read_probe_blocks();
+  return b > 0 ? b : DCP_ERR_HIP;
+}
+
+int dcp_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* digest, int32_t digest_len, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || digest_len < 1) return DCP_ERR_INVALID_ARG;
+  if (bytes == 0) return DCP_OK;
+  if (!buf || !digest || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return DCP_ERR_INVALID_ARG;
+  const int blocks = hbm_read_probe_blocks();
+  if (blocks < 1) return DCP_ERR_HIP;
+  if (digest_len < blocks) return DCP_ERR_INVALID_ARG;
+  return launch_hbm_read_probe(buf, bytes, digest, blocks, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? DCP_OK
+             : DCP_ERR_HIP;
+}
+
 int dcp_profile_enable(int on) {
   g_prof.on = on != 0;
   g_prof.used = 0;

@@ -74,6 +74,11 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_lse, int num_
                             int num_heads, int head_dim_v, const float* sink, int out_dtype,
                             void* out_o, float* out_lse, hipStream_t s);
 
+// Streaming-read probe (probe.hip): workgroups it launches on the current
+// device, and the launch (bytes a multiple of 16, buf 16-byte aligned).
+int hbm_read_probe_blocks();
+hipError_t launch_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* digest, int blocks, hipStream_t s);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

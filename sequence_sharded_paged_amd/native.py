@@ -27,6 +27,7 @@ EXPORTS = [
     "dcp_kv_cache_write", "dcp_partial_verify_attn_workspace_size", "dcp_partial_verify_attn",
     "dcp_partial_segment_attn_workspace_size", "dcp_partial_segment_attn", "dcp_gather_context",
     "dcp_profile_enable", "dcp_profile_collect", "dcp_check_block_table", "dcp_partial_decode_attn_noalloc",
+    "dcp_hbm_read_probe_blocks", "dcp_hbm_read_probe",
 ]
 
 
@@ -100,6 +101,10 @@ def lib():
         L.dcp_profile_enable.argtypes = [ctypes.c_int]
         L.dcp_profile_collect.restype = ctypes.c_int
         L.dcp_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+        L.dcp_hbm_read_probe_blocks.restype = ctypes.c_int
+        L.dcp_hbm_read_probe_blocks.argtypes = []
+        L.dcp_hbm_read_probe.restype = ctypes.c_int
+        L.dcp_hbm_read_probe.argtypes = [vp, i64, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -319,6 +324,20 @@ def dcp_gather_context(kv: KvCache, dcp_size, interleave, block_table, cu_ctx, t
     _check("dcp_gather_context", lib().dcp_gather_context(
         ctypes.byref(kv), dcp_size, interleave, _ptr(block_table), block_table.shape[0], block_table.stride(0),
         max_vblocks, _ptr(cu_ctx), int(total_tokens), _ptr(out_k), _ptr(out_v), _stream(stream)))
+
+
+def dcp_hbm_read_probe_blocks() -> int:
+    n = lib().dcp_hbm_read_probe_blocks()
+    if n < 1:
+        raise DcpError("dcp_hbm_read_probe_blocks", n)
+    return n
+
+
+def dcp_hbm_read_probe(buf, digest, stream=None):
+    """Read every byte of the device tensor ``buf`` once; ``digest`` (uint32 /
+    int32, >= dcp_hbm_read_probe_blocks() entries) receives each workgroup's XOR."""
+    _check("dcp_hbm_read_probe", lib().dcp_hbm_read_probe(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(digest), digest.numel(), _stream(stream)))
 
 
 def dcp_profile_enable(on: bool = True):

@@ -226,6 +226,20 @@ def test_segment_validation(L):
         assert call(lens=NULL, algo=algo) == INV
 
 
+def test_hbm_read_probe_validation(L):
+    p = _fake(64)
+    aligned = ctypes.c_void_p((p.value + 15) // 16 * 16)   # (never dereferenced: every call below is refused)
+    f = L.dcp_hbm_read_probe
+    assert f(p, 0, p, 1, NULL) == 0                  # nothing to read: nothing launched
+    assert f(p, 24, p, 8, NULL) == INV               # not a multiple of 16 bytes
+    assert f(p, -16, p, 8, NULL) == INV
+    assert f(p, 32, p, 0, NULL) == INV               # no digest entries
+    assert f(NULL, 32, p, 8, NULL) == INV
+    assert f(aligned, 32, NULL, 8, NULL) == INV
+    misaligned = ctypes.c_void_p(aligned.value + 4)
+    assert f(misaligned, 32, p, 8, NULL) == INV
+
+
 def test_gather_validation(L):
     p = _fake(64)
     f = L.dcp_gather_context
