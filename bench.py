@@ -70,8 +70,9 @@ GATHER_METRIC = "context gather GB/s (stored rows read + written) at 1 GPU"
 KERNEL_NAMES = {"gqa": "gqa_attn_kernel", "mla": "mla_attn_kernel", "generic": "generic_attn_kernel",
                 "kv_write": "kv_write", "gather": "gather_context_kernel"}
 # Sources compiled into each kernel family (the attention kernels include the
-# split-KV header, which fixes their workspace layout).
-KERNEL_SOURCES = {"gqa": ["attn_gqa.hip", "splitkv.h"], "mla": ["attn_mla.hip", "splitkv.h"],
+# split-KV header, which fixes their workspace layout, and through it the
+# 64-bit half split and join).
+KERNEL_SOURCES = {"gqa": ["attn_gqa.hip", "splitkv.h", "halves.h"], "mla": ["attn_mla.hip", "splitkv.h", "halves.h"],
                   "generic": ["attn_generic.hip"], "kv_write": ["kv_write.hip"], "gather": ["gather.hip"]}
 
 

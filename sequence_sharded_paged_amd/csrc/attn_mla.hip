@@ -144,12 +144,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int kImm>
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
   static_assert(kImm >= 0 && kImm < 4096, "global offset immediate");
-  // (readfirstlane yields a signed int: each half is taken as uint32_t before
-  // widening, or a low word with bit 31 set would smear into the high word)
   const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
-  const uint64_t bu = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  const uint64_t bu = join_halves(__builtin_amdgcn_readfirstlane(low_half(b)), __builtin_amdgcn_readfirstlane(high_half(b)));
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff),
                "s"(reinterpret_cast<const void*>(bu)), "s"(__builtin_amdgcn_readfirstlane(lds_base - kImm)), "i"(kImm)
                : "memory", "m0");

@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "halves.h"
 
 namespace dcp {
 
@@ -162,10 +163,11 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
   return v;
 }
 
+// A wave-uniform copy of v (through the 32-bit broadcast, half by half).
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  const uint64_t u = static_cast<uint64_t>(v);
+  return static_cast<int64_t>(
+      join_halves(__builtin_amdgcn_readfirstlane(low_half(u)), __builtin_amdgcn_readfirstlane(high_half(u))));
 }
 
 // Where a worker starts (wave-uniform values).
